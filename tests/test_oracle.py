@@ -1,0 +1,545 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Every pin below checks the oracle against a closed form, an invariant that
+the definition implies, a 60-digit brute force on tiny inputs, a library
+routine used as an independent route, or a value worked by hand.  The
+mutation test at the end plants plausible mistakes in the oracle and checks
+that at least one pin fails for each.
+"""
+import decimal
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import attention as A
+from oracle import numerics as N
+from oracle import ring as R
+from oracle import schedule as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ---------------------------------------------------------------------------
+# attention pins
+# ---------------------------------------------------------------------------
+
+def brute_force_attention(q, K, V, scale):
+    """Per-row, pure Python, 60 significant digits, no max subtraction."""
+    ctx = decimal.Context(prec=60)
+    out, lses = [], []
+    for qi in q:
+        w = []
+        for kj in K:
+            s = ctx.multiply(decimal.Decimal(scale),
+                             sum((decimal.Decimal(a) * decimal.Decimal(b) for a, b in zip(qi, kj)),
+                                 decimal.Decimal(0)))
+            w.append(ctx.exp(s))
+        z = sum(w, decimal.Decimal(0))
+        row = []
+        for d in range(len(V[0])):
+            num = sum((w[j] * decimal.Decimal(V[j][d]) for j in range(len(K))), decimal.Decimal(0))
+            row.append(float(ctx.divide(num, z)))
+        out.append(row)
+        lses.append(float(ctx.ln(z)))
+    return np.array(out), np.array(lses)
+
+
+def pin_brute_force():
+    rng = _rng(1)
+    for n, L, D in [(1, 1, 1), (3, 5, 4), (4, 9, 8), (2, 7, 3)]:
+        q = rng.standard_normal((n, D))
+        K = rng.standard_normal((L, D)) * 2
+        V = rng.standard_normal((L, D + 1))
+        sc = 1 / math.sqrt(D)
+        o, l = A.softmax_attention(q, K, V, sc)
+        ob, lb = brute_force_attention(q.tolist(), K.tolist(), V.tolist(), sc)
+        assert np.allclose(o, ob, rtol=0, atol=1e-12), np.abs(o - ob).max()
+        assert np.allclose(l, lb, rtol=0, atol=1e-12)
+
+
+def pin_two_key_closed_form():
+    # two keys: o = sigmoid(d) v1 + sigmoid(-d) v2 with d = scale (q.k1 - q.k2)
+    rng = _rng(2)
+    q = rng.standard_normal((5, 6))
+    K = rng.standard_normal((2, 6))
+    V = rng.standard_normal((2, 3))
+    sc = 0.37
+    o, lse = A.softmax_attention(q, K, V, sc)
+    d = sc * (q @ K[0] - q @ K[1])
+    sig = 1 / (1 + np.exp(-d))
+    exp_o = sig[:, None] * V[0] + (1 - sig)[:, None] * V[1]
+    assert np.allclose(o, exp_o, atol=1e-13)
+    s1, s2 = sc * q @ K[0], sc * q @ K[1]
+    assert np.allclose(lse, np.logaddexp(s1, s2), atol=1e-13)
+
+
+def pin_weights_sum_to_one():
+    # with V = identity the output rows are the weights themselves
+    rng = _rng(3)
+    L = 13
+    q = rng.standard_normal((7, 5)) * 3
+    K = rng.standard_normal((L, 5)) * 3
+    o, _ = A.softmax_attention(q, K, np.eye(L), 1.0)
+    assert np.all(o >= 0)
+    assert np.allclose(o.sum(axis=1), 1.0, atol=1e-12)
+    # and they are the softmax of the scores (library routine as the other route)
+    assert np.allclose(o, scipy.special.softmax(q @ K.T, axis=1), atol=1e-12)
+
+
+def pin_key_permutation_invariance():
+    rng = _rng(4)
+    q = rng.standard_normal((6, 8))
+    K = rng.standard_normal((20, 8))
+    V = rng.standard_normal((20, 8))
+    perm = rng.permutation(20)
+    o1, l1 = A.softmax_attention(q, K, V, 0.3)
+    o2, l2 = A.softmax_attention(q, K[perm], V[perm], 0.3)
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+
+
+def pin_uniform_when_q_zero():
+    rng = _rng(5)
+    K = rng.standard_normal((11, 4))
+    V = rng.standard_normal((11, 4))
+    o, lse = A.softmax_attention(np.zeros((2, 4)), K, V, 1.0)
+    assert np.allclose(o, V.mean(axis=0), atol=1e-13)
+    assert np.allclose(lse, math.log(11), atol=1e-13)
+
+
+def pin_needle():
+    rng = _rng(6)
+    D, L = 8, 30
+    q = rng.standard_normal((1, D))
+    K = rng.standard_normal((L, D)) * 0.01
+    V = rng.standard_normal((L, D))
+    K[17] = 500 * q[0] / np.linalg.norm(q[0])
+    o, _ = A.softmax_attention(q, K, V, 1.0)
+    assert np.array_equal(o[0], V[17]) or np.allclose(o[0], V[17], rtol=0, atol=1e-300)
+
+
+def _tiny_ring_setup(seed=7, slot_tokens=6, lens=(6, 5, 6, 4), heads=2, D=4, text=3):
+    rng = _rng(seed)
+    ring = R.RingModel(n_slots=5, slot_tokens=slot_tokens, heads=heads, head_dim=D, dtype="f32")
+    blocks = []
+    for n in lens:
+        k = rng.standard_normal((n, heads, D)).astype(np.float32)
+        v = rng.standard_normal((n, heads, D)).astype(np.float32)
+        ring.append(k, v, n)
+        blocks.append((k, v))
+    tring = R.RingModel(n_slots=1, slot_tokens=8, heads=heads, head_dim=D, dtype="f32")
+    tk = rng.standard_normal((text, heads, D)).astype(np.float32)
+    tv = rng.standard_normal((text, heads, D)).astype(np.float32)
+    tring.append(tk, tv, text)
+    return rng, ring, tring, blocks, (tk, tv)
+
+
+def pin_full_prefix_equivalence():
+    # A video of 4 tiny blocks; the last block's queries over the cache holding
+    # the whole prefix equal plain full attention over the concatenated sequence,
+    # restricted to that block's rows (computed here by the 60-digit brute force).
+    rng, ring, tring, blocks, (tk, tv) = _tiny_ring_setup()
+    H, D = 2, 4
+    n3 = blocks[3][0].shape[0]
+    q = rng.standard_normal((1, n3, H, D))
+    meta = {"q_len": n3, "segs": [(0, 6), (1, 5), (2, 6), (3, 4)], "text_slot": 0, "text_len": 3}
+    out, lse = A.block_attention_ref(q, ring, tring, [meta], scale=0.5)
+    for h in range(H):
+        Kf = np.concatenate([b[0][:, h, :] for b in blocks] + [tk[:, h, :]]).astype(np.float64)
+        Vf = np.concatenate([b[1][:, h, :] for b in blocks] + [tv[:, h, :]]).astype(np.float64)
+        ob, lb = brute_force_attention(q[0, :, h, :].tolist(), Kf.tolist(), Vf.tolist(), 0.5)
+        assert np.allclose(out[0, :, h, :], ob, atol=1e-12)
+        assert np.allclose(lse[0, h, :], lb, atol=1e-12)
+
+
+def pin_key_set_order_and_lengths():
+    rng, ring, tring, blocks, (tk, tv) = _tiny_ring_setup()
+    meta = {"q_len": 1, "segs": [(2, 3), (0, 6)], "text_slot": 0, "text_len": 2}
+    K, V = A.key_set(ring, tring, meta, 1)
+    expK = np.concatenate([blocks[2][0][:3, 1], blocks[0][0][:6, 1], tk[:2, 1]])
+    expV = np.concatenate([blocks[2][1][:3, 1], blocks[0][1][:6, 1], tv[:2, 1]])
+    assert np.array_equal(K, expK.astype(np.float64))
+    assert np.array_equal(V, expV.astype(np.float64))
+
+
+def pin_tokens_past_length_ignored():
+    rng, ring, tring, blocks, _ = _tiny_ring_setup()
+    q = rng.standard_normal((1, 3, 2, 4))
+    meta = {"q_len": 3, "segs": [(0, 2), (1, 5)], "text_slot": 0, "text_len": 1}
+    o1, _ = A.block_attention_ref(q, ring, tring, [meta])
+    # overwrite everything past the lengths; the result must not move
+    k0 = blocks[0][0].copy(); v0 = blocks[0][1].copy()
+    k0[2:] = 99.0; v0[2:] = -99.0
+    ring.append(k0, v0, 6, slot=0)
+    tk = np.full((3, 2, 4), 50.0, np.float32); tv = np.full((3, 2, 4), 7.0, np.float32)
+    tk[0] = tring.keys(0, 0, 1)[0][None].astype(np.float32).repeat(1, 0)
+    tk[0, 1] = tring.keys(0, 1, 1)[0]
+    tv[0, 0] = tring.values(0, 0, 1)[0]
+    tv[0, 1] = tring.values(0, 1, 1)[0]
+    tring.append(tk, tv, 3, slot=0)
+    o2, _ = A.block_attention_ref(q, ring, tring, [meta])
+    assert np.array_equal(o1, o2)
+
+
+def pin_default_scale():
+    rng, ring, tring, _, _ = _tiny_ring_setup()
+    q = rng.standard_normal((1, 4, 2, 4))
+    meta = {"q_len": 4, "segs": [(1, 5), (3, 4)], "text_slot": 0, "text_len": 3}
+    o1, l1 = A.block_attention_ref(q, ring, tring, [meta])
+    o2, l2 = A.block_attention_ref(q, ring, tring, [meta], scale=0.5)  # 1/sqrt(4)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o3, _ = A.block_attention_ref(q, ring, tring, [meta], scale=0.25)
+    assert not np.allclose(o1, o3)
+
+
+def pin_rows_and_heads_subset():
+    rng, ring, tring, _, _ = _tiny_ring_setup()
+    q = rng.standard_normal((2, 5, 2, 4))
+    metas = [{"q_len": 5, "segs": [(0, 6), (1, 5)], "text_slot": 0, "text_len": 3},
+             {"q_len": 3, "segs": [(2, 6)], "text_slot": 0, "text_len": 0}]
+    o, l = A.block_attention_ref(q, ring, tring, metas)
+    os_, ls = A.block_attention_ref(q, ring, tring, metas, heads=[1], rows=[0, 4])
+    # BLAS may take another summation path for fewer rows: equal to rounding
+    assert np.allclose(os_[0, [0, 4], 1], o[0, [0, 4], 1], rtol=0, atol=1e-14)
+    assert np.allclose(os_[1, [0], 1], o[1, [0], 1], rtol=0, atol=1e-14)
+    assert np.isnan(os_[1, 4]).all() and np.isnan(o[1, 3:]).all()
+    assert np.isnan(os_[0, :, 0]).all()
+
+
+def pin_lse():
+    rng = _rng(9)
+    q = rng.standard_normal((4, 6))
+    K = rng.standard_normal((25, 6)) * 4
+    V = rng.standard_normal((25, 6))
+    _, lse = A.softmax_attention(q, K, V, 0.9)
+    assert np.allclose(lse, scipy.special.logsumexp(0.9 * q @ K.T, axis=1), atol=1e-12)
+
+
+ATTENTION_PINS = [pin_brute_force, pin_two_key_closed_form, pin_weights_sum_to_one,
+                  pin_key_permutation_invariance, pin_uniform_when_q_zero, pin_needle,
+                  pin_full_prefix_equivalence, pin_key_set_order_and_lengths,
+                  pin_tokens_past_length_ignored, pin_default_scale,
+                  pin_rows_and_heads_subset, pin_lse]
+
+
+# ---------------------------------------------------------------------------
+# ring pins
+# ---------------------------------------------------------------------------
+
+def pin_ring_fifo_wraps():
+    ring = R.RingModel(3, 4, 1, 2, "bf16")
+    slots = [ring.append(np.full((4, 1, 2), i, np.uint16), np.full((4, 1, 2), i, np.uint16), 4)
+             for i in range(7)]
+    assert slots == [0, 1, 2, 0, 1, 2, 0] and ring.appended == 7
+    assert ring.append(np.ones((4, 1, 2), np.uint16), np.ones((4, 1, 2), np.uint16), 2, slot=2) == 2
+    assert ring.appended == 7
+
+
+def pin_ring_layout_golden():
+    with open(os.path.join(GOLDEN, "ring_layout_tiny.json")) as f:
+        g = json.load(f)
+    ring = R.RingModel(**g["ring"], dtype="bf16")
+    assert ring.mem.size == g["total_elems"] and ring.t_pad == 64
+    # write distinct codes so every element is identifiable
+    H, D = g["ring"]["heads"], g["ring"]["head_dim"]
+    for s in range(g["ring"]["n_slots"]):
+        t = np.arange(5)[:, None, None]; h = np.arange(H)[None, :, None]; d = np.arange(D)[None, None, :]
+        k = (1 + s * 1000 + t * 100 + h * 10 + d).astype(np.uint16)
+        v = (20000 + s * 1000 + t * 100 + h * 10 + d).astype(np.uint16)
+        ring.append(k, v, 5, slot=s)
+    for e in g["k"]:
+        assert ring.mem[e["offset"]] == 1 + e["s"] * 1000 + e["t"] * 100 + e["h"] * 10 + e["d"]
+    for e in g["v"]:
+        assert ring.mem[e["offset"]] == 20000 + e["s"] * 1000 + e["t"] * 100 + e["h"] * 10 + e["d"]
+
+
+def pin_ring_roundtrip_and_zero_tail():
+    rng = _rng(11)
+    ring = R.RingModel(2, 70, 3, 8, "bf16")
+    assert ring.t_pad == 128
+    k = rng.integers(1, 60000, (70, 3, 8)).astype(np.uint16)
+    v = rng.integers(1, 60000, (70, 3, 8)).astype(np.uint16)
+    ring.append(k, v, 70, slot=1)
+    k2 = rng.integers(1, 60000, (70, 3, 8)).astype(np.uint16)
+    ring.append(k2, k2, 33, slot=1)   # shorter append: tokens 33.. become zero
+    for h in range(3):
+        assert np.array_equal(ring.keys(1, h, 33), N.bf16_bits_to_f64(k2[:33, h]))
+        assert np.array_equal(ring.values(1, h, 33), N.bf16_bits_to_f64(k2[:33, h]))
+        assert not ring.keys(1, h, 128)[33:].any() and not ring.values(1, h, 128)[33:].any()
+    assert not ring.mem[: ring.mem.size // 2].any()   # slot 0 untouched
+
+
+def pin_ring_loop_writer():
+    # element-by-element writer in plain loops gives the same bytes
+    rng = _rng(12)
+    S_, T, H, D = 2, 3, 2, 2
+    ring = R.RingModel(S_, T, H, D, "bf16")
+    k = rng.integers(1, 999, (T, H, D)).astype(np.uint16)
+    v = rng.integers(1, 999, (T, H, D)).astype(np.uint16)
+    ring.append(k, v, T, slot=1)
+    ref = np.zeros(S_ * 2 * H * 64 * D, np.uint16)
+    for t in range(T):
+        for h in range(H):
+            for d in range(D):
+                ref[(((1 * 2) + 0) * H + h) * 64 * D + t * D + d] = k[t, h, d]
+                ref[(((1 * 2) + 1) * H + h) * 64 * D + d * 64 + t] = v[t, h, d]
+    assert np.array_equal(ring.mem, ref)
+
+
+RING_PINS = [pin_ring_fifo_wraps, pin_ring_layout_golden, pin_ring_roundtrip_and_zero_tail,
+             pin_ring_loop_writer]
+
+
+# ---------------------------------------------------------------------------
+# schedule pins
+# ---------------------------------------------------------------------------
+
+def pin_alpha_bar_start_and_product():
+    ab = S.alpha_bar(1000, 1e-4, 0.02)
+    assert ab[0] == 1.0 and ab[1] == 1.0 - 1e-4
+    b = np.array([1e-4 + (0.02 - 1e-4) * i / 999 for i in range(1000)])
+    other = np.exp(np.cumsum(np.log1p(-b)))          # a different route: sum of logs
+    assert np.allclose(ab[1:], other, rtol=1e-12, atol=0)
+    assert np.all(np.diff(ab) < 0)
+    assert abs(ab[1000] - 4.035830e-5) < 5e-11
+
+
+def pin_betas_linear():
+    b = S.betas(1000, 1e-4, 0.02)
+    assert b[0] == 1e-4 and abs(b[-1] - 0.02) < 1e-18
+    assert np.allclose(np.diff(b), (0.02 - 1e-4) / 999, rtol=1e-9)
+
+
+def pin_two_step_schedule_by_hand():
+    # T = 2, betas (0.1, 0.3): abar_1 = 0.9, abar_2 = 0.63.  A step from t=2 to
+    # t'=0 returns x0_hat = (x - sqrt(0.37) eps) / sqrt(0.63).
+    ab = S.alpha_bar(2, 0.1, 0.3)
+    assert abs(ab[1] - 0.9) < 1e-15 and abs(ab[2] - 0.63) < 1e-15
+    x, e = 1.25, -0.5
+    got = S.ddim_step(np.array([x]), np.array([e]), 2, 0, ab)[0]
+    assert abs(got - (1.25 + 0.5 * math.sqrt(0.37)) / math.sqrt(0.63)) < 1e-14
+    # t=2 -> t'=1: sqrt(0.9) x0_hat + sqrt(0.1) eps
+    got = S.ddim_step(np.array([x]), np.array([e]), 2, 1, ab)[0]
+    x0 = (1.25 + 0.5 * math.sqrt(0.37)) / math.sqrt(0.63)
+    assert abs(got - (math.sqrt(0.9) * x0 - 0.5 * math.sqrt(0.1))) < 1e-14
+
+
+def pin_ddim_consistency():
+    # x on the forward-process line of (x0, eps) stays on it after a step
+    ab = S.alpha_bar(1000, 1e-4, 0.02)
+    rng = _rng(13)
+    x0 = rng.standard_normal(100)
+    eps = rng.standard_normal(100)
+    for t in [1, 20, 143, 500, 999, 1000]:
+        tp = S.prev_timestep(t, 20)
+        x = math.sqrt(ab[t]) * x0 + math.sqrt(1 - ab[t]) * eps
+        exp = math.sqrt(ab[tp]) * x0 + math.sqrt(1 - ab[tp]) * eps
+        assert np.allclose(S.ddim_step(x, eps, t, tp, ab), exp, atol=1e-10)
+
+
+def pin_trajectory_recovers_x0():
+    ab = S.alpha_bar(1000, 1e-4, 0.02)
+    rng = _rng(14)
+    x0 = rng.standard_normal(50)
+    eps = rng.standard_normal(50)
+    x = math.sqrt(ab[1000]) * x0 + math.sqrt(1 - ab[1000]) * eps
+    t = 1000
+    while t > 0:
+        tp = S.prev_timestep(t, 20)
+        x = S.ddim_step(x, eps, t, tp, ab)
+        t = tp
+    assert np.allclose(x, x0, atol=1e-9)
+
+
+def pin_identity_and_coefficients():
+    ab = S.alpha_bar(1000, 1e-4, 0.02)
+    rng = _rng(15)
+    x = rng.standard_normal(64)
+    e = rng.standard_normal(64)
+    for t in [0, 7, 500]:
+        assert np.allclose(S.ddim_step(x, e, t, t, ab), x, atol=1e-14)
+        c1, c2 = S.ddim_coefficients(t, t, ab)
+        assert abs(c1 - 1) < 1e-15 and abs(c2) < 1e-15
+    for t in [1, 143, 1000]:
+        tp = S.prev_timestep(t, 20)
+        c1, c2 = S.ddim_coefficients(t, tp, ab)
+        assert np.allclose(c1 * x + c2 * e, S.ddim_step(x, e, t, tp, ab), atol=1e-13)
+        assert c1 >= 1.0 and c2 < 0
+
+
+def pin_prev_timestep():
+    assert S.prev_timestep(1000, 20) == 980 and S.prev_timestep(15, 20) == 0
+    assert S.prev_timestep(20, 20) == 0 and S.prev_timestep(0, 20) == 0
+
+
+def pin_bf16_rounding():
+    cases = {1.0: 0x3F80, 1 + 2 ** -8: 0x3F80, 1 + 3 * 2 ** -8: 0x3F82,
+             1 + 2 ** -8 + 2 ** -40: 0x3F81, -2.0: 0xC000, 0.0: 0x0000,
+             3.5e38: 0x7F80, 2.0 ** -133: 0x0001, 2.0 ** -134: 0x0000,
+             1.5 * 2.0 ** -133: 0x0002}
+    for x, bits in cases.items():
+        assert int(N.f64_to_bf16_bits(np.array([x]))[0]) == bits, (x, hex(bits))
+    # on fp32-representable values, single rounding equals torch's fp32 -> bf16
+    x = _rng(16).standard_normal(20000).astype(np.float32) * 7
+    tb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(N.f64_to_bf16_bits(x.astype(np.float64)), tb)
+    assert np.array_equal(N.bf16_bits_to_f64(tb), torch.from_numpy(tb.view(np.int16)).view(
+        torch.bfloat16).to(torch.float64).numpy())
+
+
+def pin_block_update_rounding():
+    ab = S.alpha_bar(1000, 1e-4, 0.02)
+    rng = _rng(17)
+    x = N.f64_to_bf16_bits(rng.standard_normal((2, 300)))
+    e = N.f64_to_bf16_bits(rng.standard_normal((2, 300)))
+    out = S.block_update_ref(x, e, [500, 0])
+    assert np.array_equal(out[1], x[1])    # t = 0: t' = 0, identity
+    exact = S.ddim_step(N.bf16_bits_to_f64(x[0]), N.bf16_bits_to_f64(e[0]), 500, 480, ab)
+    got = N.bf16_bits_to_f64(out[0])
+    assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-30)
+
+
+SCHEDULE_PINS = [pin_alpha_bar_start_and_product, pin_betas_linear, pin_two_step_schedule_by_hand,
+                 pin_ddim_consistency, pin_trajectory_recovers_x0, pin_identity_and_coefficients,
+                 pin_prev_timestep, pin_bf16_rounding, pin_block_update_rounding]
+
+ALL_PINS = ATTENTION_PINS + RING_PINS + SCHEDULE_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin()
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must make at least one pin fail
+# ---------------------------------------------------------------------------
+
+def _mut_drop_text(orig):
+    def key_set(ring, text_ring, meta, head):
+        m = dict(meta); m["text_len"] = 0
+        return orig(ring, text_ring, m, head)
+    return key_set
+
+
+def _mut_seg_off_by_one(orig):
+    def key_set(ring, text_ring, meta, head):
+        m = dict(meta); m["segs"] = [(s, max(n - 1, 1)) for s, n in meta["segs"]]
+        return orig(ring, text_ring, m, head)
+    return key_set
+
+
+def _mut_values_are_keys(orig):
+    def key_set(ring, text_ring, meta, head):
+        K, V = orig(ring, text_ring, meta, head)
+        return K, K.copy()
+    return key_set
+
+
+def _mut_scale(orig):
+    def block_attention_ref(q, ring, text_ring, metas, scale=None, heads=None, rows=None):
+        if scale is None:
+            scale = 1.0 / q.shape[-1]
+        return orig(q, ring, text_ring, metas, scale, heads, rows)
+    return block_attention_ref
+
+
+def _mut_softmax_axis(orig):
+    # normalises over the queries instead of over the keys
+    def softmax_attention(q, k, v, scale, chunk=256):
+        s = scale * (np.asarray(q) @ np.asarray(k).T)
+        e = np.exp(s - s.max(axis=0, keepdims=True))
+        o = (e / e.sum(axis=0, keepdims=True)) @ np.asarray(v)
+        return o, scipy.special.logsumexp(s, axis=1)
+    return softmax_attention
+
+
+def _mut_lse_no_max(orig):
+    def softmax_attention(q, k, v, scale, chunk=256):
+        o, lse = orig(q, k, v, scale, chunk)
+        s = scale * (np.asarray(q) @ np.asarray(k).T)
+        return o, lse - s.max(axis=1)
+    return softmax_attention
+
+
+def _mut_ring_v_not_transposed(orig_cls):
+    class Mut(orig_cls):
+        def v_offset(self, s, h, t, d):
+            H, D, T = self.heads, self.head_dim, self.t_pad
+            return ((s * 2 + 1) * H + h) * T * D + t * D + d
+    return Mut
+
+
+def _mut_ring_fifo(orig_cls):
+    class Mut(orig_cls):
+        def append(self, k, v, n_tokens, slot=None):
+            if slot is None:
+                slot = min(self.appended, self.n_slots - 1)
+                self.appended += 1
+            return orig_cls.append(self, k, v, n_tokens, slot)
+    return Mut
+
+
+def _mut_abar_index(orig):
+    def alpha_bar(T, b0, b1):
+        ab = orig(T, b0, b1)
+        return np.concatenate([[1.0, 1.0], ab[1:-1]])
+    return alpha_bar
+
+
+def _mut_c2_sign(orig):
+    def ddim_step(x, eps, t, t_prev, ab):
+        x = np.asarray(x, dtype=np.float64); eps = np.asarray(eps, dtype=np.float64)
+        x0 = (x + np.sqrt(1.0 - ab[t]) * eps) / np.sqrt(ab[t])
+        return np.sqrt(ab[t_prev]) * x0 + np.sqrt(1.0 - ab[t_prev]) * eps
+    return ddim_step
+
+
+def _mut_no_clamp(orig):
+    return lambda t, stride: int(t) - int(stride)
+
+
+def _mut_round_truncate(orig):
+    def f64_to_bf16_bits(x):
+        f = np.asarray(x, dtype=np.float64).astype(np.float32)
+        return (f.view(np.uint32) >> 16).astype(np.uint16)
+    return f64_to_bf16_bits
+
+
+MUTATIONS = [
+    (A, "key_set", _mut_drop_text),
+    (A, "key_set", _mut_seg_off_by_one),
+    (A, "key_set", _mut_values_are_keys),
+    (A, "block_attention_ref", _mut_scale),
+    (A, "softmax_attention", _mut_softmax_axis),
+    (A, "softmax_attention", _mut_lse_no_max),
+    (R, "RingModel", _mut_ring_v_not_transposed),
+    (R, "RingModel", _mut_ring_fifo),
+    (S, "alpha_bar", _mut_abar_index),
+    (S, "ddim_step", _mut_c2_sign),
+    (S, "prev_timestep", _mut_no_clamp),
+    (N, "f64_to_bf16_bits", _mut_round_truncate),
+]
+
+
+@pytest.mark.parametrize("mod,name,mut", MUTATIONS, ids=lambda x: getattr(x, "__name__", str(x)))
+def test_planted_mistake_is_caught(monkeypatch, mod, name, mut):
+    monkeypatch.setattr(mod, name, mut(getattr(mod, name)))
+    if mod is N:   # rounding is also imported by name into the schedule module
+        monkeypatch.setattr(S, name, getattr(N, name))
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception:  # noqa: BLE001  (a crash counts as caught, too)
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake {mut.__name__} passed every pin"
