@@ -1,0 +1,229 @@
+"""Benchmark of the block-wise attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one queued block of the
+480p video-DiT workload (24 heads x 64, 5400 queries = 4 latent frames of
+30x45 tokens, keys = 5400 cached neighbouring-block + 5400 own + 226 text):
+  1. ba_cache_append   the block's K/V into its ring slot
+  2. ba_block_attention  queries over [cached block | own block | text]
+  3. ba_block_update   the block's latents, DDIM step at t = 500
+Inputs are seeded synthetic tensors (N(0,1)*0.5 bf16 for Q/K/V, N(0,1) for
+latents and noise) already resident in HBM when the timed region starts.
+
+Prints one JSON line.  `value` is block-attention TFLOP/s over the whole
+step (algorithmic FLOPs 4*Lq*Lk*D*H over valid keys / step time).  The
+`roofline` object rates the attention kernel alone against the bf16 dense
+MFMA peak, from HIP events around each of its launches on the launch stream.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+PEAK_HBM_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "block_wise_long_amd", "csrc", "attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_d64_dit480p_traffic.md")
+
+
+def kernel_hash():
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload_name):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on another version of the kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_sha256_16:\s*([0-9a-f]+)", text)
+    w = re.search(r"workload:\s*(\S+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m and b and w) or m.group(1) != kernel_hash() or w.group(1) != workload_name:
+        return None
+    return float(b.group(1))
+
+
+def cpu_baseline(cfg, inputs, budget_s):
+    """The oracle, as it stands, on whole heads of the workload until the
+    time budget is used (at least one head)."""
+    from oracle import attention as A
+    from oracle import numerics as N
+    from oracle import ring as R
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    ring = R.RingModel(cfg.n_slots, cfg.slot_tokens, cfg.heads, cfg.head_dim, cfg.dtype)
+    ring.append(inputs["k_ctx"][0], inputs["v_ctx"][0], cfg.ctx_len)
+    ring.append(inputs["k_cur"][0], inputs["v_cur"][0], cfg.cur_len)
+    text = R.RingModel(1, cfg.text_len, cfg.heads, cfg.head_dim, cfg.dtype)
+    text.append(inputs["k_text"], inputs["v_text"], cfg.text_len)
+    q = N.decode(inputs["q"], cfg.dtype)
+    meta = [{"q_len": cfg.q_len, "segs": list(cfg.segs[0]), "text_slot": 0, "text_len": cfg.text_len}]
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < cfg.heads:
+        A.block_attention_ref(q, ring, text, meta, heads=[heads])
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * cfg.q_len * cfg.key_len * cfg.head_dim * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {cfg.heads} heads, all {cfg.q_len} queries over all {cfg.key_len} keys, "
+                      f"fp64 numpy (BLAS dgemm), {dt:.1f} s wall"}
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size: under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE readings give the counters' scale (bytes moved
+    per KiB reported)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="config index (1 is the default bench line)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import block_wise_long_amd as B
+    from workloads import CONFIGS, make_attention_inputs, make_update_inputs
+
+    cfg = CONFIGS[args.workload]
+    if cfg.n_blocks != 1 or cfg.full_sequence or cfg.dtype != "bf16":
+        print(json.dumps({"error": "bench steps cover the single-block bf16 workloads (1, 2)"}))
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    inputs = make_attention_inputs(cfg)
+    upd = make_update_inputs(cfg, inputs["_rng"])
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    H, D = cfg.heads, cfg.head_dim
+    ring = B.ba_ring_init(cfg.n_slots, cfg.slot_tokens, H, D, B.BA_BF16)
+    text = B.ba_ring_init(1, cfg.text_len, H, D, B.BA_BF16)
+    B.ba_cache_append(ring, dev(inputs["k_ctx"][0]), dev(inputs["v_ctx"][0]), cfg.ctx_len)
+    k_cur = dev(inputs["k_cur"])          # [1][L][H][D]
+    v_cur = dev(inputs["v_cur"])
+    B.ba_cache_append(text, dev(inputs["k_text"]), dev(inputs["v_text"]), cfg.text_len)
+    q = dev(inputs["q"])
+    out = torch.empty_like(q)
+    x = dev(upd["x"])
+    eps = dev(upd["eps"])
+    ts = [int(t) for t in upd["t"]]
+    cur_slot = cfg.segs[0][1][0]
+    metas = [B.make_meta(cfg.q_len, list(cfg.segs[0]), 0, cfg.text_len)]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.ba_cache_append_batched(ring, k_cur, v_cur, [cur_slot])
+        if ev is not None:
+            ev[1].record(stream)
+        B.ba_block_attention(q, ring, text, metas, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+        B.ba_block_update(x, eps, ts)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, bracketed by synchronisation
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_append = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_attn_all = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_attn = float(np.mean(ms_attn_all))
+    ms_update = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    flops = float(cfg.flops())
+    tflops_step = flops / (ms_step * 1e-3) / 1e12
+    tflops_attn = flops / (ms_attn * 1e-3) / 1e12
+    append_bytes = 2.0 * 2 * cfg.cur_len * H * D * 2    # read K,V + write K,V (valid tokens)
+    update_bytes = 3.0 * cfg.update_elems * 2
+    traffic = traffic_from_profile(cfg.name)
+
+    res = {
+        "metric": "block-attention TFLOP/s + % bf16 MFMA peak; latent frames/s at 1 GPU",
+        "value": round(tflops_step, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "n_blocks": cfg.n_blocks, "heads": H, "head_dim": D,
+                   "queries": cfg.q_len, "keys": cfg.key_len,
+                   "key_segments": [cfg.ctx_len, cfg.cur_len, cfg.text_len],
+                   "latent_frames_per_step": cfg.latent_frames},
+        "pct_bf16_peak_step": round(100 * tflops_step / PEAK_BF16_TFLOPS, 2),
+        "latent_frames_per_s": round(cfg.latent_frames / (ms_step * 1e-3), 1),
+        "kernel_ms": {"append": round(ms_append, 5), "attention": round(ms_attn, 5),
+                      "attention_p10": round(float(np.percentile(ms_attn_all, 10)), 5),
+                      "attention_p90": round(float(np.percentile(ms_attn_all, 90)), 5),
+                      "update": round(ms_update, 5)},
+        "append_GBs": round(append_bytes / (ms_append * 1e-3) / 1e9, 1),
+        "update_GBs": round(update_bytes / (ms_update * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops_attn, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops_attn / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": f"attention_bf16_kernel<{D}>",
+                     "flop_per_launch": flops},
+    }
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

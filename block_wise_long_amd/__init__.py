@@ -1,0 +1,263 @@
+"""Python binding of libblockattn (argument marshalling only).
+
+Each function has the name of the C entry point it calls (see
+include/blockattn.h) and takes torch tensors for device buffers; every step
+of the computation runs in the library's HIP kernels.  The stream is torch's
+current stream.  There is no fallback: importing this package fails when
+libblockattn.so has not been built (python -m block_wise_long_amd.build).
+"""
+import ctypes
+import os
+import re
+
+# torch ships its own HIP runtime (libamdhip64.so.7).  Load it first so that
+# the library's dependency on that soname resolves to the same copy: two HIP
+# runtimes in one process do not share devices, memory or streams.
+import torch  # noqa: F401  (load order matters, see above)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libblockattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "blockattn.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m block_wise_long_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+BA_OK, BA_ERR_INVALID_ARG, BA_ERR_UNSUPPORTED, BA_ERR_OUT_OF_RANGE, BA_ERR_HIP = range(5)
+BA_BF16, BA_F32 = 0, 1
+BA_TOKEN_ALIGN = 64
+BA_MAX_SEGS = 8
+
+
+class ba_ring(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
+                ("slot_tokens", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("slot_stride_tokens", ctypes.c_int32), ("appended", ctypes.c_int64)]
+
+
+class ba_seg(ctypes.Structure):
+    _fields_ = [("slot", ctypes.c_int32), ("len", ctypes.c_int32)]
+
+
+class ba_block_meta(ctypes.Structure):
+    _fields_ = [("q_len", ctypes.c_int32), ("n_segs", ctypes.c_int32),
+                ("seg", ba_seg * BA_MAX_SEGS), ("text_slot", ctypes.c_int32),
+                ("text_len", ctypes.c_int32)]
+
+
+class ba_schedule(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("stride", ctypes.c_int32),
+                ("beta_start", ctypes.c_double), ("beta_end", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SIGS = {
+    "ba_ring_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
+    "ba_ring_init": (_I32, [ctypes.POINTER(ba_ring), _P, ctypes.c_size_t, _I32, _I32, _I32, _I32, _I32, _P]),
+    "ba_cache_append": (_I32, [ctypes.POINTER(ba_ring), _P, _P, _I32, ctypes.POINTER(_I32), _P]),
+    "ba_cache_append_batched": (_I32, [ctypes.POINTER(ba_ring), _P, _P, _I32, ctypes.POINTER(_I32), _I32, _P]),
+    "ba_block_attention": (_I32, [_P, _I32, ctypes.POINTER(ba_ring), ctypes.POINTER(ba_ring),
+                                  ctypes.POINTER(ba_block_meta), _I32, ctypes.c_float, _P, _P, _P]),
+    "ba_block_update": (_I32, [_P, _P, _I64, ctypes.POINTER(_I32), _I32, ctypes.POINTER(ba_schedule), _P]),
+    "ba_schedule_coefficients": (_I32, [ctypes.POINTER(ba_schedule), ctypes.POINTER(_I32), _I32,
+                                        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
+    "ba_status_string": (ctypes.c_char_p, [_I32]),
+    "ba_last_error": (ctypes.c_char_p, []),
+    "ba_version": (_I32, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+raw = _lib   # the C entry points themselves, for callers that marshal by hand
+
+
+def header_symbols():
+    """Names of the functions include/blockattn.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b(ba_\w+)\s*\(", text, re.M)))
+
+
+class BlockAttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.ba_last_error().decode()
+        super().__init__(f"{where}: {_lib.ba_status_string(status).decode()}: {msg}")
+
+
+def _check(status, where):
+    if status != BA_OK:
+        raise BlockAttnError(status, where)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+
+    if t.dtype == torch.bfloat16:
+        return BA_BF16
+    if t.dtype == torch.float32:
+        return BA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def ba_status_string(status):
+    return _lib.ba_status_string(status).decode()
+
+
+def ba_last_error():
+    return _lib.ba_last_error().decode()
+
+
+def ba_version():
+    return _lib.ba_version()
+
+
+def ba_ring_bytes(n_slots, slot_tokens, heads, head_dim, dtype=BA_BF16):
+    return _lib.ba_ring_bytes(n_slots, slot_tokens, heads, head_dim, dtype)
+
+
+class Ring:
+    """A ba_ring descriptor plus the torch buffer that backs it."""
+
+    def __init__(self, desc, buffer):
+        self.desc = desc
+        self.buffer = buffer
+
+    @property
+    def appended(self):
+        return self.desc.appended
+
+    @property
+    def slot_stride_tokens(self):
+        return self.desc.slot_stride_tokens
+
+
+def ba_ring_init(n_slots, slot_tokens, heads, head_dim, dtype=BA_BF16, device="cuda"):
+    """Allocate (via torch) and initialise a zero-filled ring; returns a Ring."""
+
+    nbytes = ba_ring_bytes(n_slots, slot_tokens, heads, head_dim, dtype)
+    if nbytes == 0:
+        # let the library produce the precise error
+        desc = ba_ring()
+        _check(_lib.ba_ring_init(ctypes.byref(desc), None, 0, n_slots, slot_tokens, heads,
+                                 head_dim, dtype, None), "ba_ring_init")
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    view = buf[off:off + nbytes]
+    desc = ba_ring()
+    _check(_lib.ba_ring_init(ctypes.byref(desc), ctypes.c_void_p(view.data_ptr()), nbytes, n_slots,
+                             slot_tokens, heads, head_dim, dtype, _stream()), "ba_ring_init")
+    return Ring(desc, view)
+
+
+def ba_cache_append(ring, k, v, n_tokens=None):
+    """FIFO append of k, v ([n_tokens][heads][head_dim]); returns the slot written."""
+    n = k.shape[0] if n_tokens is None else n_tokens
+    _shape_check(ring, k, v, n, 1)
+    slot = _I32(-1)
+    _check(_lib.ba_cache_append(ctypes.byref(ring.desc), _dev(k, "k"), _dev(v, "v"), n,
+                                ctypes.byref(slot), _stream()), "ba_cache_append")
+    return slot.value
+
+
+def ba_cache_append_batched(ring, k, v, slots):
+    """k, v: [n_blocks][n_tokens][heads][head_dim]; block i -> slots[i]."""
+    nb = len(slots)
+    n = k.shape[1]
+    _shape_check(ring, k, v, n, nb)
+    arr = (_I32 * max(nb, 1))(*slots)
+    _check(_lib.ba_cache_append_batched(ctypes.byref(ring.desc), _dev(k, "k"), _dev(v, "v"), n,
+                                        arr, nb, _stream()), "ba_cache_append_batched")
+
+
+def _shape_check(ring, k, v, n, nb):
+    d = ring.desc
+    want = n * d.heads * d.head_dim * nb
+    if k.numel() < want or v.numel() < want:
+        raise ValueError("k/v smaller than n_blocks * n_tokens * heads * head_dim")
+    if _dtype_code(k) != d.dtype or _dtype_code(v) != d.dtype:
+        raise TypeError("k/v dtype differs from the ring's")
+
+
+def make_meta(q_len, segs, text_slot=0, text_len=0):
+    """One ba_block_meta from (slot, len) segments."""
+    if len(segs) > BA_MAX_SEGS:
+        raise ValueError("too many segments")
+    m = ba_block_meta()
+    m.q_len, m.n_segs, m.text_slot, m.text_len = q_len, len(segs), text_slot, text_len
+    for i, (s, n) in enumerate(segs):
+        m.seg[i].slot, m.seg[i].len = s, n
+    return m
+
+
+def ba_block_attention(q, cache, text, metas, scale=0.0, out=None, lse=None):
+    """q: [n_blocks][q_stride][heads][head_dim]; metas: list of ba_block_meta
+    or dicts (q_len, segs, text_slot, text_len).  Returns out (allocated if
+    not given); lse, when given, is filled in."""
+
+    nb, q_stride = q.shape[0], q.shape[1]
+    if q.shape[2] != cache.desc.heads or q.shape[3] != cache.desc.head_dim:
+        raise ValueError("q shape does not match the cache ring")
+    if len(metas) != nb:
+        raise ValueError("one meta per block")
+    arr = (ba_block_meta * max(nb, 1))()
+    for i, m in enumerate(metas):
+        arr[i] = m if isinstance(m, ba_block_meta) else make_meta(
+            m["q_len"], m["segs"], m.get("text_slot", 0), m.get("text_len", 0))
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is not None and (lse.dtype != torch.float32 or lse.numel() < nb * cache.desc.heads * q_stride):
+        raise ValueError("lse must be fp32 [n_blocks][heads][q_stride]")
+    _check(_lib.ba_block_attention(_dev(q, "q"), q_stride, ctypes.byref(cache.desc),
+                                   ctypes.byref(text.desc) if text is not None else None,
+                                   arr, nb, float(scale), _dev(out, "out"),
+                                   _dev(lse, "lse") if lse is not None else None, _stream()),
+           "ba_block_attention")
+    return out
+
+
+def _schedule(s):
+    if s is None:
+        return None
+    if isinstance(s, ba_schedule):
+        return ctypes.byref(s)
+    return ctypes.byref(ba_schedule(s.get("T", 1000), s.get("stride", 20),
+                                    s.get("beta_start", 1e-4), s.get("beta_end", 0.02)))
+
+
+def ba_block_update(x, eps, t_per_block, schedule=None):
+    """In place on x ([n_blocks][elems] bf16) with eps of the same shape."""
+    nb = len(t_per_block)
+    if x.shape != eps.shape or x.shape[0] != nb:
+        raise ValueError("x, eps must be [n_blocks][elems] with one timestep per block")
+    elems = x.numel() // max(nb, 1)
+    arr = (_I32 * max(nb, 1))(*[int(t) for t in t_per_block])
+    _check(_lib.ba_block_update(_dev(x, "x"), _dev(eps, "eps"), elems, arr, nb, _schedule(schedule),
+                                _stream()), "ba_block_update")
+    return x
+
+
+def ba_schedule_coefficients(t, schedule=None):
+    """Host-only: the fp32 (c1, c2) lists ba_block_update applies."""
+    n = len(t)
+    arr = (_I32 * max(n, 1))(*[int(v) for v in t])
+    c1 = (ctypes.c_float * max(n, 1))()
+    c2 = (ctypes.c_float * max(n, 1))()
+    _check(_lib.ba_schedule_coefficients(_schedule(schedule), arr, n, c1, c2), "ba_schedule_coefficients")
+    return list(c1)[:n], list(c2)[:n]

@@ -1,0 +1,358 @@
+// C-ABI entry points of libblockattn: argument checks on the host, launch
+// geometry, and the fp64 noise-schedule coefficients of the block update.
+// Every check runs before anything is enqueued; on failure nothing is
+// enqueued, no descriptor changes and ba_last_error() says why.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "blockattn.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ba_status fail(ba_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ba_status ok() {
+  g_err[0] = '\0';
+  return BA_OK;
+}
+
+ba_status hip_fail(hipError_t e, const char* what) {
+  return fail(BA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == BA_BF16 ? 2 : (dtype == BA_F32 ? 4 : 0); }
+
+int64_t pad_tokens(int64_t t) {
+  return (t + ba::kTokenAlign - 1) / ba::kTokenAlign * ba::kTokenAlign;
+}
+
+ba_status check_shape(int32_t n_slots, int32_t slot_tokens, int32_t heads, int32_t head_dim,
+                      int32_t dtype) {
+  if (dtype != BA_BF16 && dtype != BA_F32) return fail(BA_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(BA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (n_slots < 1 || slot_tokens < 1 || heads < 1)
+    return fail(BA_ERR_INVALID_ARG, "n_slots, slot_tokens and heads must be >= 1");
+  if (heads > 65535) return fail(BA_ERR_OUT_OF_RANGE, "heads %d > 65535", heads);
+  if (slot_tokens > (1 << 30)) return fail(BA_ERR_OUT_OF_RANGE, "slot_tokens too large");
+  return BA_OK;
+}
+
+ba_status check_ring(const ba_ring* r, const char* name) {
+  if (r == nullptr) return fail(BA_ERR_INVALID_ARG, "%s is NULL", name);
+  ba_status st = check_shape(r->n_slots, r->slot_tokens, r->heads, r->head_dim, r->dtype);
+  if (st != BA_OK) return st;
+  if (r->base == nullptr) return fail(BA_ERR_INVALID_ARG, "%s->base is NULL", name);
+  if (!aligned(r->base, 256)) return fail(BA_ERR_INVALID_ARG, "%s->base not 256-byte aligned", name);
+  if (r->slot_stride_tokens != pad_tokens(r->slot_tokens))
+    return fail(BA_ERR_INVALID_ARG, "%s was not set up by ba_ring_init", name);
+  if (r->appended < 0) return fail(BA_ERR_INVALID_ARG, "%s->appended < 0", name);
+  return BA_OK;
+}
+
+void schedule_or_default(const ba_schedule* s, ba_schedule* out) {
+  if (s) {
+    *out = *s;
+  } else {
+    out->T = 1000;
+    out->stride = 20;
+    out->beta_start = 1e-4;
+    out->beta_end = 0.02;
+  }
+}
+
+ba_status check_schedule(const ba_schedule& s) {
+  if (s.T < 2 || s.T > 100000) return fail(BA_ERR_OUT_OF_RANGE, "schedule T=%d outside [2, 100000]", s.T);
+  if (s.stride < 0) return fail(BA_ERR_OUT_OF_RANGE, "schedule stride < 0");
+  if (!(s.beta_start > 0.0) || !(s.beta_end >= s.beta_start) || !(s.beta_end < 1.0))
+    return fail(BA_ERR_OUT_OF_RANGE, "need 0 < beta_start <= beta_end < 1");
+  return BA_OK;
+}
+
+// abar_0..abar_T of the DDPM linear beta schedule, in fp64.
+std::vector<double> alpha_bar(const ba_schedule& s) {
+  std::vector<double> ab(s.T + 1);
+  ab[0] = 1.0;
+  double acc = 1.0;
+  for (int i = 1; i <= s.T; ++i) {
+    const double beta = s.beta_start + (s.beta_end - s.beta_start) * (double)(i - 1) / (double)(s.T - 1);
+    acc *= 1.0 - beta;
+    ab[i] = acc;
+  }
+  return ab;
+}
+
+// DDIM (eta = 0) from t to t' = max(t - stride, 0), folded into x' = c1 x + c2 eps.
+void coefficients(const std::vector<double>& ab, int stride, int t, float* c1, float* c2) {
+  const int tp = t - stride > 0 ? t - stride : 0;
+  const double at = ab[t], ap = ab[tp];
+  *c1 = (float)sqrt(ap / at);
+  *c2 = (float)(sqrt(1.0 - ap) - sqrt(ap) * sqrt(1.0 - at) / sqrt(at));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ba_status_string(ba_status s) {
+  switch (s) {
+    case BA_OK: return "BA_OK";
+    case BA_ERR_INVALID_ARG: return "BA_ERR_INVALID_ARG";
+    case BA_ERR_UNSUPPORTED: return "BA_ERR_UNSUPPORTED";
+    case BA_ERR_OUT_OF_RANGE: return "BA_ERR_OUT_OF_RANGE";
+    case BA_ERR_HIP: return "BA_ERR_HIP";
+  }
+  return "BA_ERR_UNKNOWN";
+}
+
+const char* ba_last_error(void) { return g_err; }
+
+int32_t ba_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+size_t ba_ring_bytes(int32_t n_slots, int32_t slot_tokens, int32_t heads, int32_t head_dim,
+                     int32_t dtype) {
+  if (check_shape(n_slots, slot_tokens, heads, head_dim, dtype) != BA_OK) return 0;
+  return (size_t)n_slots * 2 * heads * (size_t)pad_tokens(slot_tokens) * head_dim * elem_bytes(dtype);
+}
+
+ba_status ba_ring_init(ba_ring* ring, void* base, size_t bytes, int32_t n_slots, int32_t slot_tokens,
+                       int32_t heads, int32_t head_dim, int32_t dtype, hipStream_t stream) {
+  if (ring == nullptr) return fail(BA_ERR_INVALID_ARG, "ring is NULL");
+  ba_status st = check_shape(n_slots, slot_tokens, heads, head_dim, dtype);
+  if (st != BA_OK) return st;
+  if (base == nullptr) return fail(BA_ERR_INVALID_ARG, "base is NULL");
+  if (!aligned(base, 256)) return fail(BA_ERR_INVALID_ARG, "base not 256-byte aligned");
+  const size_t need = ba_ring_bytes(n_slots, slot_tokens, heads, head_dim, dtype);
+  if (bytes < need) return fail(BA_ERR_INVALID_ARG, "ring buffer has %zu bytes, needs %zu", bytes, need);
+  hipError_t e = ba::launch_zero_fill(base, need, stream);
+  if (e != hipSuccess) return hip_fail(e, "zero fill launch");
+  ring->base = base;
+  ring->n_slots = n_slots;
+  ring->slot_tokens = slot_tokens;
+  ring->heads = heads;
+  ring->head_dim = head_dim;
+  ring->dtype = dtype;
+  ring->slot_stride_tokens = (int32_t)pad_tokens(slot_tokens);
+  ring->appended = 0;
+  return ok();
+}
+
+static ba_status append_common(const ba_ring* ring, const void* k, const void* v, int32_t n_tokens,
+                               const int32_t* slots, int32_t n_blocks, hipStream_t stream) {
+  ba_status st = check_ring(ring, "ring");
+  if (st != BA_OK) return st;
+  if (k == nullptr || v == nullptr) return fail(BA_ERR_INVALID_ARG, "k or v is NULL");
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(BA_ERR_INVALID_ARG, "k or v not 16-byte aligned");
+  if (n_tokens < 1 || n_tokens > ring->slot_tokens)
+    return fail(BA_ERR_OUT_OF_RANGE, "n_tokens %d outside [1, %d]", n_tokens, ring->slot_tokens);
+  for (int i = 0; i < n_blocks; ++i) {
+    if (slots[i] < 0 || slots[i] >= ring->n_slots)
+      return fail(BA_ERR_OUT_OF_RANGE, "slot %d outside [0, %d)", slots[i], ring->n_slots);
+    for (int j = 0; j < i; ++j)
+      if (slots[j] == slots[i]) return fail(BA_ERR_INVALID_ARG, "slot %d written twice in one call", slots[i]);
+  }
+  const int eb = elem_bytes(ring->dtype);
+  const int64_t block_elems = (int64_t)n_tokens * ring->heads * ring->head_dim;
+  for (int first = 0; first < n_blocks; first += ba::kAppendMaxBlocks) {
+    ba::AppendArgs a;
+    memset(&a, 0, sizeof(a));
+    a.n_blocks = n_blocks - first < ba::kAppendMaxBlocks ? n_blocks - first : ba::kAppendMaxBlocks;
+    a.k = static_cast<const char*>(k) + first * block_elems * eb;
+    a.v = static_cast<const char*>(v) + first * block_elems * eb;
+    a.ring = ring->base;
+    a.n_tokens = n_tokens;
+    a.heads = ring->heads;
+    a.t_pad = ring->slot_stride_tokens;
+    for (int i = 0; i < a.n_blocks; ++i) a.slot[i] = slots[first + i];
+    hipError_t e = ba::launch_append(a, ring->head_dim, eb, stream);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+  }
+  return ok();
+}
+
+ba_status ba_cache_append(ba_ring* ring, const void* k, const void* v, int32_t n_tokens,
+                          int32_t* slot_out, hipStream_t stream) {
+  ba_status st = check_ring(ring, "ring");
+  if (st != BA_OK) return st;
+  const int32_t slot = (int32_t)(ring->appended % ring->n_slots);
+  st = append_common(ring, k, v, n_tokens, &slot, 1, stream);
+  if (st != BA_OK) return st;
+  ring->appended += 1;
+  if (slot_out) *slot_out = slot;
+  return ok();
+}
+
+ba_status ba_cache_append_batched(const ba_ring* ring, const void* k, const void* v, int32_t n_tokens,
+                                  const int32_t* slots, int32_t n_blocks, hipStream_t stream) {
+  if (n_blocks < 0) return fail(BA_ERR_INVALID_ARG, "n_blocks < 0");
+  if (n_blocks > 0 && slots == nullptr) return fail(BA_ERR_INVALID_ARG, "slots is NULL");
+  if (n_blocks > 4096) return fail(BA_ERR_OUT_OF_RANGE, "n_blocks %d > 4096", n_blocks);
+  if (n_blocks == 0) {
+    ba_status st = check_ring(ring, "ring");
+    return st != BA_OK ? st : ok();
+  }
+  return append_common(ring, k, v, n_tokens, slots, n_blocks, stream);
+}
+
+ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cache, const ba_ring* text,
+                             const ba_block_meta* meta, int32_t n_blocks, float scale, void* out,
+                             float* lse, hipStream_t stream) {
+  ba_status st = check_ring(cache, "cache");
+  if (st != BA_OK) return st;
+  if (n_blocks < 0) return fail(BA_ERR_INVALID_ARG, "n_blocks < 0");
+  if (n_blocks > 0 && meta == nullptr) return fail(BA_ERR_INVALID_ARG, "meta is NULL");
+  if (q == nullptr || out == nullptr) return fail(BA_ERR_INVALID_ARG, "q or out is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(BA_ERR_INVALID_ARG, "q or out not 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(BA_ERR_INVALID_ARG, "lse not 4-byte aligned");
+  if (q_stride < 1) return fail(BA_ERR_INVALID_ARG, "q_stride < 1");
+  if (!isfinite(scale)) return fail(BA_ERR_INVALID_ARG, "scale is not finite");
+  bool need_text = false;
+  for (int b = 0; b < n_blocks; ++b) need_text |= meta[b].text_len != 0;
+  if (text != nullptr || need_text) {
+    if (need_text && text == nullptr) return fail(BA_ERR_INVALID_ARG, "text_len > 0 but text ring is NULL");
+    st = check_ring(text, "text");
+    if (st != BA_OK) return st;
+    if (text->heads != cache->heads || text->head_dim != cache->head_dim || text->dtype != cache->dtype)
+      return fail(BA_ERR_INVALID_ARG, "text ring heads/head_dim/dtype differ from the cache ring");
+  }
+  const int D = cache->head_dim;
+  const int H = cache->heads;
+  if ((int64_t)n_blocks * q_stride * H > (int64_t)1 << 40) return fail(BA_ERR_OUT_OF_RANGE, "q too large");
+
+  // host-side segment tables (zero-length segments dropped, text last)
+  std::vector<ba::AttnBlock> blocks(n_blocks);
+  int32_t q_max = 0;
+  for (int b = 0; b < n_blocks; ++b) {
+    const ba_block_meta& m = meta[b];
+    ba::AttnBlock& B = blocks[b];
+    memset(&B, 0, sizeof(B));
+    if (m.q_len < 0 || m.q_len > q_stride)
+      return fail(BA_ERR_OUT_OF_RANGE, "block %d: q_len %d outside [0, %d]", b, m.q_len, q_stride);
+    if (m.n_segs < 0 || m.n_segs > BA_MAX_SEGS)
+      return fail(BA_ERR_OUT_OF_RANGE, "block %d: n_segs %d outside [0, %d]", b, m.n_segs, BA_MAX_SEGS);
+    B.q_len = m.q_len;
+    int64_t keys = 0;
+    for (int i = 0; i < m.n_segs; ++i) {
+      const ba_seg& sg = m.seg[i];
+      if (sg.slot < 0 || sg.slot >= cache->n_slots)
+        return fail(BA_ERR_OUT_OF_RANGE, "block %d seg %d: slot %d outside [0, %d)", b, i, sg.slot, cache->n_slots);
+      if (sg.len < 0 || sg.len > cache->slot_tokens)
+        return fail(BA_ERR_OUT_OF_RANGE, "block %d seg %d: len %d outside [0, %d]", b, i, sg.len, cache->slot_tokens);
+      if (sg.len == 0) continue;
+      B.slot[B.n_segs] = sg.slot;
+      B.len[B.n_segs] = sg.len;
+      ++B.n_segs;
+      keys += sg.len;
+    }
+    if (m.text_len != 0) {
+      if (m.text_len < 0 || m.text_len > text->slot_tokens)
+        return fail(BA_ERR_OUT_OF_RANGE, "block %d: text_len %d outside [0, %d]", b, m.text_len, text->slot_tokens);
+      if (m.text_slot < 0 || m.text_slot >= text->n_slots)
+        return fail(BA_ERR_OUT_OF_RANGE, "block %d: text_slot %d outside [0, %d)", b, m.text_slot, text->n_slots);
+      B.slot[B.n_segs] = -1 - m.text_slot;
+      B.len[B.n_segs] = m.text_len;
+      ++B.n_segs;
+      keys += m.text_len;
+    }
+    if (m.q_len > 0 && keys == 0) return fail(BA_ERR_INVALID_ARG, "block %d has queries but no keys", b);
+    if (m.q_len > q_max) q_max = m.q_len;
+  }
+  if (n_blocks == 0 || q_max == 0) return ok();
+
+  const bool bf16 = cache->dtype == BA_BF16;
+  const int qtile = bf16 ? ba::attention_bf16_q_tile() : ba::attention_f32_q_tile();
+  const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
+  const int eb = elem_bytes(cache->dtype);
+  for (int first = 0; first < n_blocks; first += ba::kAttnMaxBlocks) {
+    const int nb = n_blocks - first < ba::kAttnMaxBlocks ? n_blocks - first : ba::kAttnMaxBlocks;
+    ba::AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    int32_t qm = 0;
+    for (int i = 0; i < nb; ++i) {
+      a.blk[i] = blocks[first + i];
+      if (a.blk[i].q_len > qm) qm = a.blk[i].q_len;
+    }
+    if (qm == 0) continue;
+    const int64_t blk_elems = (int64_t)q_stride * H * D;
+    a.q = static_cast<const char*>(q) + first * blk_elems * eb;
+    a.out = static_cast<char*>(out) + first * blk_elems * eb;
+    a.lse = lse ? lse + (int64_t)first * H * q_stride : nullptr;
+    a.cache = cache->base;
+    a.text = text ? text->base : nullptr;
+    a.cache_tpad = cache->slot_stride_tokens;
+    a.text_tpad = text ? text->slot_stride_tokens : 0;
+    a.q_stride = q_stride;
+    a.heads = H;
+    a.n_qtiles = (qm + qtile - 1) / qtile;
+    const int64_t total = (int64_t)nb * H * a.n_qtiles;
+    if (total > (int64_t)1 << 30) return fail(BA_ERR_OUT_OF_RANGE, "too many attention tasks");
+    a.total_tasks = (int32_t)total;
+    a.tasks_per_xcd = (a.total_tasks + 7) / 8;
+    a.qscale = (float)((double)sc * 1.4426950408889634);
+    a.scale_ln = sc;
+    hipError_t e = bf16 ? ba::launch_attention_bf16(a, D, stream) : ba::launch_attention_f32(a, D, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+  }
+  return ok();
+}
+
+ba_status ba_schedule_coefficients(const ba_schedule* sched, const int32_t* t, int32_t n, float* c1, float* c2) {
+  ba_schedule s;
+  schedule_or_default(sched, &s);
+  ba_status st = check_schedule(s);
+  if (st != BA_OK) return st;
+  if (n < 0) return fail(BA_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && (t == nullptr || c1 == nullptr || c2 == nullptr))
+    return fail(BA_ERR_INVALID_ARG, "t, c1 or c2 is NULL");
+  for (int i = 0; i < n; ++i)
+    if (t[i] < 0 || t[i] > s.T) return fail(BA_ERR_OUT_OF_RANGE, "t[%d] = %d outside [0, %d]", i, t[i], s.T);
+  const std::vector<double> ab = alpha_bar(s);
+  for (int i = 0; i < n; ++i) coefficients(ab, s.stride, t[i], &c1[i], &c2[i]);
+  return ok();
+}
+
+ba_status ba_block_update(void* x, const void* eps, int64_t elems_per_block, const int32_t* t_per_block,
+                          int32_t n_blocks, const ba_schedule* sched, hipStream_t stream) {
+  if (n_blocks < 0) return fail(BA_ERR_INVALID_ARG, "n_blocks < 0");
+  if (elems_per_block < 0) return fail(BA_ERR_INVALID_ARG, "elems_per_block < 0");
+  if (n_blocks > 0 && t_per_block == nullptr) return fail(BA_ERR_INVALID_ARG, "t_per_block is NULL");
+  if (x == nullptr || eps == nullptr) return fail(BA_ERR_INVALID_ARG, "x or eps is NULL");
+  if (!aligned(x, 16) || !aligned(eps, 16)) return fail(BA_ERR_INVALID_ARG, "x or eps not 16-byte aligned");
+  if (n_blocks > 65535) return fail(BA_ERR_OUT_OF_RANGE, "n_blocks %d > 65535", n_blocks);
+  std::vector<float> c1(n_blocks), c2(n_blocks);
+  ba_status st = ba_schedule_coefficients(sched, t_per_block, n_blocks, c1.data(), c2.data());
+  if (st != BA_OK) return st;
+  if (n_blocks == 0 || elems_per_block == 0) return ok();
+  for (int first = 0; first < n_blocks; first += ba::kUpdateMaxBlocks) {
+    ba::UpdateArgs a;
+    memset(&a, 0, sizeof(a));
+    a.n_blocks = n_blocks - first < ba::kUpdateMaxBlocks ? n_blocks - first : ba::kUpdateMaxBlocks;
+    a.x = static_cast<uint16_t*>(x) + first * elems_per_block;
+    a.eps = static_cast<const uint16_t*>(eps) + first * elems_per_block;
+    a.elems = elems_per_block;
+    for (int i = 0; i < a.n_blocks; ++i) {
+      a.c1[i] = c1[first + i];
+      a.c2[i] = c2[first + i];
+    }
+    hipError_t e = ba::launch_update(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "update launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function the header declares, sizes rings like the oracle's model,
+computes the update coefficients like the oracle, and rejects bad arguments
+before it would enqueue anything.  No call here reaches a kernel launch."""
+import ctypes
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import block_wise_long_amd as B
+from oracle import ring as oring
+from oracle import schedule as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dereferenced
+
+
+def test_exports_every_declared_symbol():
+    names = B.header_symbols()
+    assert len(names) == 10
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert B.ba_version() == 10000
+
+
+@pytest.mark.parametrize("shape", [(2, 5400, 24, 64), (16, 5400, 24, 64), (2, 7800, 40, 128), (1, 226, 24, 64),
+                                   (3, 1, 1, 64), (5, 65, 3, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ring_bytes_match_model(shape, dtype):
+    code = B.BA_BF16 if dtype == "bf16" else B.BA_F32
+    assert B.ba_ring_bytes(*shape, code) == oring.RingModel(*shape, dtype).nbytes()
+
+
+def test_ring_bytes_rejects():
+    assert B.ba_ring_bytes(0, 10, 1, 64, 0) == 0
+    assert B.ba_ring_bytes(1, 10, 1, 96, 0) == 0
+    assert B.ba_ring_bytes(1, 10, 1, 64, 7) == 0
+
+
+def test_schedule_coefficients_match_oracle_golden():
+    with open(os.path.join(GOLDEN, "ddim_coefficients.json")) as f:
+        g = json.load(f)
+    ts = [r["t"] for r in g["coefficients"]]
+    c1, c2 = B.ba_schedule_coefficients(ts)
+    for r, a, b in zip(g["coefficients"], c1, c2):
+        assert a == np.float32(r["c1"]), (r["t"], a, r["c1"])
+        assert abs(b - np.float32(r["c2"])) <= abs(np.spacing(np.float32(r["c2"]))), (r["t"], b, r["c2"])
+
+
+def test_schedule_coefficients_custom_schedule():
+    sched = {"T": 50, "stride": 3, "beta_start": 1e-3, "beta_end": 0.05}
+    ab = S.alpha_bar(50, 1e-3, 0.05)
+    ts = list(range(0, 51))
+    c1, c2 = B.ba_schedule_coefficients(ts, sched)
+    for t, a, b in zip(ts, c1, c2):
+        e1, e2 = S.ddim_coefficients(t, S.prev_timestep(t, 3), ab)
+        assert abs(a - e1) <= 1e-6 * abs(e1) and abs(b - e2) <= 1e-6 * abs(e2) + 1e-7
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_schedule_rejects():
+    t = (ctypes.c_int32 * 1)(1001)
+    c = (ctypes.c_float * 1)()
+    assert B.raw.ba_schedule_coefficients(None, t, 1, c, c) == B.BA_ERR_OUT_OF_RANGE
+    assert "1001" in B.ba_last_error()
+    bad = B.ba_schedule(1, 20, 1e-4, 0.02)
+    assert B.raw.ba_schedule_coefficients(ctypes.byref(bad), t, 0, c, c) == B.BA_ERR_OUT_OF_RANGE
+    bad = B.ba_schedule(100, 20, 0.5, 0.1)
+    assert B.raw.ba_schedule_coefficients(ctypes.byref(bad), t, 0, c, c) == B.BA_ERR_OUT_OF_RANGE
+    bad = B.ba_schedule(100, -1, 1e-4, 0.02)
+    assert B.raw.ba_schedule_coefficients(ctypes.byref(bad), t, 0, c, c) == B.BA_ERR_OUT_OF_RANGE
+
+
+def _ring(n_slots=2, slot_tokens=100, heads=2, head_dim=64, dtype=0):
+    r = B.ba_ring()
+    r.base = FAKE
+    r.n_slots, r.slot_tokens, r.heads, r.head_dim, r.dtype = n_slots, slot_tokens, heads, head_dim, dtype
+    r.slot_stride_tokens = -(-slot_tokens // 64) * 64
+    r.appended = 5
+    return r
+
+
+def test_ring_init_rejects():
+    r = B.ba_ring()
+    f = B.raw.ba_ring_init
+    assert f(None, FAKE, 1 << 30, 2, 10, 1, 64, 0, None) == B.BA_ERR_INVALID_ARG
+    assert f(ctypes.byref(r), None, 1 << 30, 2, 10, 1, 64, 0, None) == B.BA_ERR_INVALID_ARG
+    assert f(ctypes.byref(r), FAKE + 16, 1 << 30, 2, 10, 1, 64, 0, None) == B.BA_ERR_INVALID_ARG
+    assert f(ctypes.byref(r), FAKE, 10, 2, 10, 1, 64, 0, None) == B.BA_ERR_INVALID_ARG
+    assert f(ctypes.byref(r), FAKE, 1 << 30, 2, 10, 1, 80, 0, None) == B.BA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(r), FAKE, 1 << 30, 2, 10, 1, 64, 3, None) == B.BA_ERR_UNSUPPORTED
+    assert r.base is None and r.n_slots == 0      # untouched on failure
+
+
+def test_append_rejects_and_leaves_ring():
+    r = _ring()
+    slot = ctypes.c_int32(-7)
+    f = B.raw.ba_cache_append
+    assert f(ctypes.byref(r), FAKE, FAKE, 101, ctypes.byref(slot), None) == B.BA_ERR_OUT_OF_RANGE
+    assert f(ctypes.byref(r), FAKE, FAKE, 0, ctypes.byref(slot), None) == B.BA_ERR_OUT_OF_RANGE
+    assert f(ctypes.byref(r), None, FAKE, 10, ctypes.byref(slot), None) == B.BA_ERR_INVALID_ARG
+    assert f(ctypes.byref(r), FAKE + 8, FAKE, 10, ctypes.byref(slot), None) == B.BA_ERR_INVALID_ARG
+    r2 = _ring(); r2.slot_stride_tokens = 100     # not from ba_ring_init
+    assert f(ctypes.byref(r2), FAKE, FAKE, 10, ctypes.byref(slot), None) == B.BA_ERR_INVALID_ARG
+    assert r.appended == 5 and slot.value == -7
+    fb = B.raw.ba_cache_append_batched
+    slots = (ctypes.c_int32 * 3)(0, 1, 0)
+    assert fb(ctypes.byref(r), FAKE, FAKE, 10, slots, 3, None) == B.BA_ERR_INVALID_ARG   # slot twice
+    slots = (ctypes.c_int32 * 2)(0, 2)
+    assert fb(ctypes.byref(r), FAKE, FAKE, 10, slots, 2, None) == B.BA_ERR_OUT_OF_RANGE
+    assert fb(ctypes.byref(r), FAKE, FAKE, 10, None, 2, None) == B.BA_ERR_INVALID_ARG
+
+
+def _meta(q_len=10, segs=((0, 50),), text_slot=0, text_len=0):
+    return B.make_meta(q_len, list(segs), text_slot, text_len)
+
+
+def _attn(cache, text, metas, q=FAKE, out=FAKE, q_stride=16, scale=0.0, lse=None):
+    arr = (B.ba_block_meta * len(metas))(*metas)
+    return B.raw.ba_block_attention(q, q_stride, ctypes.byref(cache) if cache is not None else None,
+                                    ctypes.byref(text) if text is not None else None,
+                                    arr, len(metas), scale, out, lse, None)
+
+
+def test_attention_rejects():
+    c, t = _ring(), _ring(1, 30)
+    assert _attn(None, None, [_meta()]) == B.BA_ERR_INVALID_ARG
+    assert _attn(c, None, [_meta(segs=((2, 5),))]) == B.BA_ERR_OUT_OF_RANGE          # slot
+    assert _attn(c, None, [_meta(segs=((1, 101),))]) == B.BA_ERR_OUT_OF_RANGE        # len > slot_tokens
+    assert _attn(c, None, [_meta(segs=((1, -1),))]) == B.BA_ERR_OUT_OF_RANGE
+    assert _attn(c, None, [_meta(q_len=17)]) == B.BA_ERR_OUT_OF_RANGE                # q_len > q_stride
+    assert _attn(c, None, [_meta(text_len=3)]) == B.BA_ERR_INVALID_ARG               # text missing
+    assert _attn(c, t, [_meta(text_len=31)]) == B.BA_ERR_OUT_OF_RANGE
+    assert _attn(c, t, [_meta(text_len=3, text_slot=1)]) == B.BA_ERR_OUT_OF_RANGE
+    assert _attn(c, None, [_meta(segs=((0, 0),))]) == B.BA_ERR_INVALID_ARG           # queries, no keys
+    assert _attn(c, None, [_meta()], q=FAKE + 2) == B.BA_ERR_INVALID_ARG
+    assert _attn(c, None, [_meta()], out=None) == B.BA_ERR_INVALID_ARG
+    assert _attn(c, None, [_meta()], scale=float("nan")) == B.BA_ERR_INVALID_ARG
+    assert _attn(c, _ring(1, 30, heads=3), [_meta(text_len=2)]) == B.BA_ERR_INVALID_ARG
+    m = _meta(); m.n_segs = 9
+    assert _attn(c, None, [m]) == B.BA_ERR_OUT_OF_RANGE
+    c2 = _ring(head_dim=96)
+    assert _attn(c2, None, [_meta()]) == B.BA_ERR_UNSUPPORTED
+    assert "head_dim" in B.ba_last_error()
+
+
+def test_update_rejects():
+    t = (ctypes.c_int32 * 2)(10, 2000)
+    f = B.raw.ba_block_update
+    assert f(FAKE, FAKE, 100, t, 2, None, None) == B.BA_ERR_OUT_OF_RANGE
+    t = (ctypes.c_int32 * 2)(10, -1)
+    assert f(FAKE, FAKE, 100, t, 2, None, None) == B.BA_ERR_OUT_OF_RANGE
+    t = (ctypes.c_int32 * 2)(10, 20)
+    assert f(None, FAKE, 100, t, 2, None, None) == B.BA_ERR_INVALID_ARG
+    assert f(FAKE + 2, FAKE, 100, t, 2, None, None) == B.BA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, -1, t, 2, None, None) == B.BA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 100, None, 2, None, None) == B.BA_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.ba_status_string(s).startswith("BA_")
+    assert B.ba_status_string(99) == "BA_ERR_UNKNOWN"
