@@ -122,8 +122,8 @@ def main():
     from workloads import CONFIGS, make_attention_inputs, make_update_inputs
 
     cfg = CONFIGS[args.workload]
-    if cfg.n_blocks != 1 or cfg.full_sequence or cfg.dtype != "bf16":
-        print(json.dumps({"error": "bench steps cover the single-block bf16 workloads (1, 2)"}))
+    if cfg.dtype != "bf16":
+        print(json.dumps({"error": "bench steps cover the bf16 workloads (1-4)"}))
         sys.exit(2)
     torch.cuda.set_device(0)
     inputs = make_attention_inputs(cfg)
@@ -135,23 +135,34 @@ def main():
     H, D = cfg.heads, cfg.head_dim
     ring = B.ba_ring_init(cfg.n_slots, cfg.slot_tokens, H, D, B.BA_BF16)
     text = B.ba_ring_init(1, cfg.text_len, H, D, B.BA_BF16)
-    B.ba_cache_append(ring, dev(inputs["k_ctx"][0]), dev(inputs["v_ctx"][0]), cfg.ctx_len)
-    k_cur = dev(inputs["k_cur"])          # [1][L][H][D]
-    v_cur = dev(inputs["v_cur"])
     B.ba_cache_append(text, dev(inputs["k_text"]), dev(inputs["v_text"]), cfg.text_len)
+    if cfg.full_sequence:
+        # the whole prefix is the block's own keys, one ring slot per 4-frame block
+        nseg = len(cfg.segs[0])
+        seg_len = cfg.segs[0][0][1]
+        k_cur = dev(inputs["k_cur"]).view(nseg, seg_len, H, D)
+        v_cur = dev(inputs["v_cur"]).view(nseg, seg_len, H, D)
+        cur_slots = [sl for sl, _ in cfg.segs[0]]
+    else:
+        # the neighbouring blocks' cached K/V were written by the previous step
+        B.ba_cache_append_batched(ring, dev(inputs["k_ctx"]), dev(inputs["v_ctx"]),
+                                  [sg[0][0] for sg in cfg.segs])
+        k_cur = dev(inputs["k_cur"])      # [n_blocks][L][H][D]
+        v_cur = dev(inputs["v_cur"])
+        cur_slots = [sg[1][0] for sg in cfg.segs]
     q = dev(inputs["q"])
     out = torch.empty_like(q)
     x = dev(upd["x"])
     eps = dev(upd["eps"])
     ts = [int(t) for t in upd["t"]]
-    cur_slot = cfg.segs[0][1][0]
-    metas = [B.make_meta(cfg.q_len, list(cfg.segs[0]), 0, cfg.text_len)]
+    metas = [B.make_meta(cfg.q_len, list(cfg.segs[b]), 0, cfg.text_len) for b in range(cfg.n_blocks)]
     stream = torch.cuda.current_stream()
+    appended_tokens = k_cur.shape[0] * k_cur.shape[1]
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        B.ba_cache_append_batched(ring, k_cur, v_cur, [cur_slot])
+        B.ba_cache_append_batched(ring, k_cur, v_cur, cur_slots)
         if ev is not None:
             ev[1].record(stream)
         B.ba_block_attention(q, ring, text, metas, out=out)
@@ -184,8 +195,8 @@ def main():
     flops = float(cfg.flops())
     tflops_step = flops / (ms_step * 1e-3) / 1e12
     tflops_attn = flops / (ms_attn * 1e-3) / 1e12
-    append_bytes = 2.0 * 2 * cfg.cur_len * H * D * 2    # read K,V + write K,V (valid tokens)
-    update_bytes = 3.0 * cfg.update_elems * 2
+    append_bytes = 2.0 * 2 * appended_tokens * H * D * 2    # read K,V + write K,V (valid tokens)
+    update_bytes = 3.0 * cfg.update_elems * cfg.n_blocks * 2
     traffic = traffic_from_profile(cfg.name)
 
     res = {
@@ -218,7 +229,7 @@ def main():
                      "traffic": traffic, "kernel": f"attention_bf16_kernel<{D}>",
                      "flop_per_launch": flops},
     }
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and cfg.n_blocks == 1 and not cfg.full_sequence:
         res["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_budget)
     else:
         res["cpu_baseline"] = None

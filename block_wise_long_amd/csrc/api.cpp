@@ -275,7 +275,7 @@ ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cac
   if (n_blocks == 0 || q_max == 0) return ok();
 
   const bool bf16 = cache->dtype == BA_BF16;
-  const int qtile = bf16 ? ba::attention_bf16_q_tile() : ba::attention_f32_q_tile();
+  const int qtile = bf16 ? ba::attention_bf16_q_tile(D) : ba::attention_f32_q_tile();
   const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
   const int eb = elem_bytes(cache->dtype);
   for (int first = 0; first < n_blocks; first += ba::kAttnMaxBlocks) {

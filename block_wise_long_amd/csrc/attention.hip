@@ -27,8 +27,9 @@
 //     denominator see the same weights.
 //   * K and V^T tiles of 64 keys are double-buffered in LDS with an XOR
 //     swizzle of 16-byte chunks (conflict-free ds_read_b128 for the MFMA
-//     operands); the next tile's global loads are in flight while the current
-//     tile computes.  One barrier per tile.
+//     operands).  The next tile streams from global memory straight into the
+//     other LDS buffer (global_load_lds_dwordx4, no staging registers) while
+//     the current tile computes.  One barrier per tile.
 //   * Workgroups are mapped to tasks XCD-major: the hardware deals workgroups
 //     round-robin to the 8 XCDs, so consecutive tasks (same block and head,
 //     neighbouring query tiles, hence the same K/V stream) share an XCD's L2.
@@ -47,9 +48,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kQTile = 128;        // queries per workgroup (4 waves x 32)
 constexpr int kKTile = 64;         // keys per LDS tile
-constexpr int kThreads = 256;
 constexpr float kLazyThreshold = 4096.0f;   // 2^12: bound on a tile's weight sum
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -103,76 +102,213 @@ __device__ __forceinline__ void advance(const AttnArgs& a, const AttnBlock& B, i
   }
 }
 
+// Per-wave state of the online softmax for its 32 queries.
+template <int D>
+struct WaveState {
+  f32x16 o[D / 32];    // O^T accumulator: lane owns query lane%32, 16 dims per block
+  float m_ref;         // reference maximum (exp2 domain); equal in lanes l, l^32
+  float l_sum;         // this lane's share of the weight sum
+};
+
+// Launch shape per head dim: waves per workgroup (32 queries each).  D = 64:
+// 4 waves, three workgroups per CU; D = 128: 8 waves sharing one set of LDS
+// buffers, one workgroup per CU.
+template <int D> struct Shape;
+template <> struct Shape<64> { static constexpr int NW = 4, WAVES_PER_SIMD = 3; };
+template <> struct Shape<128> { static constexpr int NW = 8, WAVES_PER_SIMD = 2; };
+
+constexpr int kBuffers = 3;   // LDS tile buffers: in use, being consumed, being filled
+
 template <int D>
 struct Tile {
+  static constexpr int NW = Shape<D>::NW;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int QTILE = NW * 32;
   static constexpr int KCH = D / 8;                  // 16-B chunks per K row
   static constexpr int K_CH = kKTile * KCH;          // chunks of the K tile
   static constexpr int V_CH = D * (kKTile / 8);      // chunks of the V^T tile
   static constexpr int CH = K_CH + V_CH;
-  static constexpr int K_LOADS = K_CH / kThreads;
-  static constexpr int LOADS = CH / kThreads;
-  static_assert(K_CH % kThreads == 0 && V_CH % kThreads == 0, "tile shape");
+  static constexpr int K_LOADS = K_CH / THREADS;
+  static constexpr int LOADS = CH / THREADS;
+  static_assert(K_CH % THREADS == 0 && V_CH % THREADS == 0, "tile shape");
 
-  // LDS chunk index of K row r, chunk c / V^T row d, chunk c (XOR swizzle).
-  static __device__ __forceinline__ int k_idx(int r, int c) { return r * KCH + (c ^ (r & 7)); }
-  static __device__ __forceinline__ int v_idx(int d, int c) { return K_CH + d * 8 + (c ^ (d & 7)); }
+  // XOR swizzle of the 16-byte chunks of a row.  A b128 LDS access is served
+  // 8 lanes per 128 bytes or 16 lanes per 256 bytes of banks; consecutive
+  // lanes of an MFMA operand read consecutive rows at the same chunk, so the
+  // swizzle must spread any 8 (128-byte rows: any 16 over a row pair)
+  // consecutive rows over distinct bank groups.
+  static __device__ __forceinline__ int row_swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+  static __device__ __forceinline__ int k_idx(int r, int c) {
+    return r * KCH + (D == 64 ? (c ^ row_swz128(r)) : (c ^ (r & 15)));
+  }
+  static __device__ __forceinline__ int v_idx(int d, int c) { return K_CH + d * 8 + (c ^ row_swz128(d)); }
 };
 
+// Stream one K tile and one V^T tile straight from global memory into an LDS
+// buffer (global_load_lds_dwordx4: lane i of a wave fills the i-th 16 bytes
+// after the wave's LDS base).  The swizzle is applied by choosing which global
+// chunk each lane fetches for its fixed LDS position.  Completion is waited
+// for with vmcnt before the barrier that publishes the buffer.
 template <int D>
-__device__ __forceinline__ void load_tile(const Cursor& c, int tid, u32x4 (&st)[Tile<D>::LOADS]) {
+__device__ __forceinline__ void load_tile(const Cursor& c, int tid, u32x4* buf) {
   using T = Tile<D>;
+  const uint16_t* kb = c.k + (int64_t)c.off * D;   // uniform tile bases
+  const uint16_t* vb = c.v + c.off;
+  const int lane = tid & 63;
+  const int wave_base = tid & ~63;
 #pragma unroll
   for (int u = 0; u < T::LOADS; ++u) {
-    const int g = tid + u * kThreads;
+    const int p0 = u * T::THREADS + wave_base;     // first LDS chunk of this wave
+    const int p = p0 + lane;
+    const uint16_t* src;
     if (u < T::K_LOADS) {
-      const int r = g / T::KCH, ch = g % T::KCH;
-      const int key = c.off + key_of_row(r);
-      st[u] = *reinterpret_cast<const u32x4*>(c.k + (int64_t)key * D + ch * 8);
+      const int r = p / T::KCH, pos = p % T::KCH;
+      const int ch = D == 64 ? (pos ^ T::row_swz128(r)) : (pos ^ (r & 15));
+      src = kb + (unsigned)(key_of_row(r) * D + ch * 8);
     } else {
-      const int gv = g - T::K_CH;
-      const int d = gv / 8, ch = gv % 8;
-      st[u] = *reinterpret_cast<const u32x4*>(c.v + (int64_t)d * c.tpad + c.off + ch * 8);
+      const int pv = p - T::K_CH;
+      const int d = pv / 8, pos = pv % 8;
+      const int ch = pos ^ T::row_swz128(d);
+      src = vb + (unsigned)(d * c.tpad + ch * 8);
     }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(buf + p0), 16, 0, 0);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(u32x4* lds, int tid, const u32x4 (&st)[Tile<D>::LOADS]) {
-  using T = Tile<D>;
-#pragma unroll
-  for (int u = 0; u < T::LOADS; ++u) {
-    const int g = tid + u * kThreads;
-    if (u < T::K_LOADS) {
-      const int r = g / T::KCH, ch = g % T::KCH;
-      lds[T::k_idx(r, ch)] = st[u];
-    } else {
-      const int gv = g - T::K_CH;
-      const int d = gv / 8, ch = gv % 8;
-      lds[T::v_idx(d, ch)] = st[u];
-    }
-  }
-}
+// Wait for this wave's outstanding global loads (including the LDS-direct ones).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float exchange_half(float x) {
   return __shfl_xor(x, 32);
 }
 
+// In-place select on a register the compiler must keep where it is: the tail
+// fix-up modifies live scores without creating a second copy at the join.
+// (Only VALU results are touched this way: a value an MFMA writes needs the
+// compiler's hazard tracking, so the accumulators are scaled in plain code.)
+__device__ __forceinline__ float mask_inplace(float x, bool keep) {
+  asm volatile("v_cndmask_b32 %0, %1, %0, %2" : "+v"(x) : "v"(-INFINITY), "s"(__builtin_amdgcn_ballot_w64(keep)));
+  return x;
+}
+
+// S^T of one 32-key group (LDS K rows 32g..32g+31) against the wave's queries.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(const AttnArgs a) {
+__device__ __forceinline__ f32x16 scores(const u32x4* L, int lane, int g, const bf16x8 (&qf)[D / 16]) {
+  using T = Tile<D>;
+  const int r = 32 * g + (lane & 31);
+  const int half = lane >> 5;
+  f32x16 s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 kf = as_bf16x8(L[T::k_idx(r, 2 * ks + half)]);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+  }
+  return s;
+}
+
+// O^T += V^T P^T for one 32-key group (LDS V^T columns 32g..32g+31).
+template <int D>
+__device__ __forceinline__ void accumulate(const u32x4* L, int lane, int g, const bf16x8 (&p)[2],
+                                           f32x16 (&o)[D / 32]) {
+  using T = Tile<D>;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int ob = 0; ob < D / 32; ++ob) {
+      const int d = 32 * ob + (lane & 31);
+      const bf16x8 vf = as_bf16x8(L[T::v_idx(d, 4 * g + 2 * k2 + half)]);
+      o[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[k2], o[ob], 0, 0, 0);
+    }
+}
+
+// Weights of one group from its shifted scores: bf16 exp2 values packed as
+// the B operand of the PV product, and their sum (from the rounded values).
+__device__ __forceinline__ float weights(const f32x16& s, float shift, bf16x8 (&p)[2]) {
+  bf16x2 ones2;
+  ones2[0] = (__bf16)1.0f;
+  ones2[1] = (__bf16)1.0f;
+  float l = 0.f;
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      bf16x2 pr;
+      pr[0] = (__bf16)__builtin_amdgcn_exp2f(s[8 * k2 + i] - shift);
+      pr[1] = (__bf16)__builtin_amdgcn_exp2f(s[8 * k2 + i + 1] - shift);
+      p[k2][i] = pr[0];
+      p[k2][i + 1] = pr[1];
+      l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l, false);
+    }
+  return l;
+}
+
+// One pipeline step for group k: the matrix cores take S^T of group k+1 and
+// O^T += V^T P^T of group k-1 while the vector ALUs turn
+// the raw scores of group k into weights.  P of group k replaces p on exit.
+// `valid` counts the group's keys that lie before its segment's end (>= 32:
+// all); keys past it get weight 0 in a fix-up that only tail groups run, so
+// the common path carries no mask.
+template <int D>
+__device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* Lp, int gp, int lane,
+                                          const bf16x8 (&qf)[D / 16], float c, const f32x16& s_in,
+                                          f32x16& s_out, bf16x8 (&p)[2], int valid, bool first,
+                                          WaveState<D>& w) {
+  constexpr int NOB = D / 32;
+  s_out = scores<D>(Ls, lane, gs, qf);
+  accumulate<D>(Lp, lane, gp, p, w.o);
+  f32x16 sc;
+  const float mneg = -w.m_ref;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(s_in[i], c, mneg);
+  float l_g = weights(sc, 0.f, p);
+  if (__builtin_expect(valid < 32, 0)) {
+    // tail group: element i is key 16(i/8) + 8*half + i%8 of the group
+    const int lim = valid - 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[i] = mask_inplace(sc[i], 16 * (i >> 3) + (i & 7) < lim);
+    l_g = weights(sc, 0.f, p);
+  }
+  // the group's weight sum bounds each weight: raise the reference when large
+  if (__builtin_expect(__any(first || l_g > kLazyThreshold), 0)) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, exchange_half(mx));
+    const float delta = first ? mx : fmaxf(mx, 0.f);
+    const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);   // O, l are 0 at first
+    w.l_sum *= alpha;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w.o[ob][i] *= alpha;
+    w.m_ref += delta;
+    l_g = weights(sc, delta, p);
+  }
+  w.l_sum += l_g;
+}
+
+template <int D>
+__global__ __launch_bounds__(Tile<D>::THREADS)
+__attribute__((amdgpu_waves_per_eu(Shape<D>::WAVES_PER_SIMD, Shape<D>::WAVES_PER_SIMD)))
+void attention_bf16_kernel(const AttnArgs a) {
   using T = Tile<D>;
   constexpr int NKS = D / 16;        // k-steps of the QK^T product
   constexpr int NOB = D / 32;        // 32-row blocks of O^T
-  __shared__ u32x4 lds[2][T::CH];
+  __shared__ u32x4 lds[kBuffers][T::CH];
 
   // ---- task (XCD-major order) ---------------------------------------------
-  const int w = blockIdx.x;
-  const int task = (w & 7) * a.tasks_per_xcd + (w >> 3);
+  const int wg = blockIdx.x;
+  const int task = (wg & 7) * a.tasks_per_xcd + (wg >> 3);
   if (task >= a.total_tasks) return;
   const int qt = task % a.n_qtiles;
   const int h = (task / a.n_qtiles) % a.heads;
   const int b = task / (a.n_qtiles * a.heads);
   const AttnBlock& B = a.blk[b];
-  const int q0 = qt * kQTile;
+  const int q0 = qt * T::QTILE;
   if (q0 >= B.q_len) return;
 
   const int tid = threadIdx.x;
@@ -182,6 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(const AttnA
   const int qrow = q0 + wave * 32 + (lane & 31);
   const bool row_ok = qrow < B.q_len;
   const int qrow_c = row_ok ? qrow : B.q_len - 1;
+  const bool active = q0 + wave * 32 < B.q_len;      // wave has queries (uniform)
 
   // ---- Q fragment: B operand of S^T = K Q^T, exactly as given ---------------
   bf16x8 qf[NKS];
@@ -194,141 +331,76 @@ __global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(const AttnA
   }
   const float c = a.qscale;
 
-  // ---- key tiles ----------------------------------------------------------
+  // ---- key tiles: 64 keys each, two 32-key groups ---------------------------
   int n_tiles = 0;
   for (int sg = 0; sg < B.n_segs; ++sg) n_tiles += (B.len[sg] + kKTile - 1) / kKTile;
 
-  Cursor cur;
-  cur.seg = 0;
-  open_segment<D>(a, B, h, cur);
-  u32x4 st[T::LOADS];
-  load_tile<D>(cur, tid, st);
-  store_tile<D>(lds[0], tid, st);
-  __syncthreads();
+  Cursor lc;                                  // cursor of the last tile loaded
+  lc.seg = 0;
+  open_segment<D>(a, B, h, lc);
+  Cursor cc = lc;                             // cursor of the tile being consumed
+  load_tile<D>(lc, tid, lds[0]);
+  if (n_tiles > 1) {
+    advance<D>(a, B, h, lc);
+    load_tile<D>(lc, tid, lds[1]);
+  }
 
-  f32x16 o[NOB];
+  {
+    // buffer 2 starts as zeros: the first step's deferred PV reads it
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < T::LOADS; ++u) lds[2][u * T::THREADS + tid] = z;
+  }
+  WaveState<D> w;
 #pragma unroll
   for (int j = 0; j < NOB; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[j][i] = 0.f;
-  float m_ref = 0.f;     // reference maximum (exp2 domain), same for lanes l, l^32
-  float l_sum = 0.f;     // this lane's share of the weight sum
+    for (int i = 0; i < 16; ++i) w.o[j][i] = 0.f;
+  w.m_ref = 0.f;
+  w.l_sum = 0.f;
+  wait_loads();
+  __syncthreads();
 
-  bf16x2 ones2;
-  ones2[0] = (__bf16)1.0f;
-  ones2[1] = (__bf16)1.0f;
-
-  Cursor nxt = cur;
-  for (int j = 0; j < n_tiles; ++j) {
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) {
-      advance<D>(a, B, h, nxt);
-      load_tile<D>(nxt, tid, st);
-    }
-    const u32x4* L = lds[j & 1];
-    const int valid = cur.len - cur.off;   // >= 1; a full tile when >= 64
-
-    // S^T for the two 32-key groups of the tile
-    f32x16 s[2];
+  // Software pipeline over 32-key groups (two per tile).  Tile t lives in
+  // buffer t % 3; tile t+2 starts loading when tile t+1 is published, after
+  // every wave has issued its last read of the buffer it overwrites.  Every
+  // step has the same shape: the first step's deferred PV multiplies zero
+  // weights with the zero-filled third buffer, and the last step's look-ahead
+  // QK^T reads whatever the next buffer holds and is discarded.
+  f32x16 sa, sb;                              // raw scores of even / odd groups
+  bf16x8 p[2];                                // weights of the previous group
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+  for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[g][i] = 0.f;
-      const int r = 32 * g + (lane & 31);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = as_bf16x8(L[T::k_idx(r, 2 * ks + half)]);
-        s[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[g], 0, 0, 0);
+    for (int i = 0; i < 8; ++i) p[k2][i] = (__bf16)0.0f;
+  if (active) sa = scores<D>(lds[0], lane, 0, qf);
+  int buf = 0;                                // buffer of the current tile
+  for (int t = 0; t < n_tiles; ++t) {
+    const int nbuf = buf == 2 ? 0 : buf + 1;
+    const int pbuf = buf == 0 ? 2 : buf - 1;
+    const int valid = cc.len - cc.off;
+    // group 2t: S of group 2t+1 (same tile), PV of group 2t-1 (previous tile)
+    if (active)
+      pipe_step<D>(lds[buf], 1, lds[pbuf], 1, lane, qf, c, sa, sb, p, valid, t == 0, w);
+    if (t + 1 < n_tiles) {
+      // publish tile t+1, start loading tile t+2 into the buffer of tile t-1
+      wait_loads();
+      __syncthreads();
+      if (t + 2 < n_tiles) {
+        advance<D>(a, B, h, lc);
+        load_tile<D>(lc, tid, lds[pbuf]);
       }
+      advance<D>(a, B, h, cc);
     }
-    // scores in the exp2 domain, relative to the reference maximum
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[g][i] = __builtin_fmaf(s[g][i], c, -m_ref);
-    if (valid < kKTile) {
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 32 * g + 16 * (i >> 3) + 8 * half + (i & 7);
-          if (key >= valid) s[g][i] = -INFINITY;
-        }
-    }
-
-    // weights, rounded to bf16, and their sum
-    bf16x8 pb[2][2];
-    float l_tile = 0.f;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          bf16x2 pr;
-          pr[0] = (__bf16)__builtin_amdgcn_exp2f(s[g][8 * k2 + i]);
-          pr[1] = (__bf16)__builtin_amdgcn_exp2f(s[g][8 * k2 + i + 1]);
-          pb[g][k2][i] = pr[0];
-          pb[g][k2][i + 1] = pr[1];
-          l_tile = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_tile, false);
-        }
-
-    // raise the reference maximum when the tile's weights got too large
-    // (always on the first tile, which sets it)
-    const bool need = (j == 0) || (l_tile > kLazyThreshold);
-    if (__any(need)) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[g][i]);
-      mx = fmaxf(mx, exchange_half(mx));
-      const float delta = (j == 0) ? mx : fmaxf(mx, 0.f);
-      if (j != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-        l_sum *= alpha;
-#pragma unroll
-        for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[ob][i] *= alpha;
-      }
-      m_ref += delta;
-      l_tile = 0.f;
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            bf16x2 pr;
-            pr[0] = (__bf16)__builtin_amdgcn_exp2f(s[g][8 * k2 + i] - delta);
-            pr[1] = (__bf16)__builtin_amdgcn_exp2f(s[g][8 * k2 + i + 1] - delta);
-            pb[g][k2][i] = pr[0];
-            pb[g][k2][i + 1] = pr[1];
-            l_tile = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_tile, false);
-          }
-    }
-    l_sum += l_tile;
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int ob = 0; ob < NOB; ++ob) {
-          const int d = 32 * ob + (lane & 31);
-          const bf16x8 vf = as_bf16x8(L[T::v_idx(d, 4 * g + 2 * k2 + half)]);
-          o[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[g][k2], o[ob], 0, 0, 0);
-        }
-
-    if (has_next) store_tile<D>(lds[(j + 1) & 1], tid, st);
-    __syncthreads();
-    cur = nxt;
+    // group 2t+1: S of group 2t+2 (next tile), PV of group 2t (this tile)
+    if (active)
+      pipe_step<D>(lds[nbuf], 0, lds[buf], 0, lane, qf, c, sb, sa, p, valid - 32, false, w);
+    buf = nbuf;
   }
+  if (active) accumulate<D>(lds[buf == 0 ? 2 : buf - 1], lane, 1, p, w.o);
 
   // ---- epilogue: normalise, round to bf16, store --------------------------
-  const float l_tot = l_sum + exchange_half(l_sum);
+  const float l_tot = w.l_sum + exchange_half(w.l_sum);
   const float inv = 1.0f / l_tot;
   if (row_ok) {
     uint16_t* op = static_cast<uint16_t*>(a.out) +
@@ -339,17 +411,17 @@ __global__ __launch_bounds__(kThreads, 2) void attention_bf16_kernel(const AttnA
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * ob + 8 * g4 + 4 * half;
         bf16x2 p01, p23;
-        p01[0] = (__bf16)(o[ob][4 * g4 + 0] * inv);
-        p01[1] = (__bf16)(o[ob][4 * g4 + 1] * inv);
-        p23[0] = (__bf16)(o[ob][4 * g4 + 2] * inv);
-        p23[1] = (__bf16)(o[ob][4 * g4 + 3] * inv);
+        p01[0] = (__bf16)(w.o[ob][4 * g4 + 0] * inv);
+        p01[1] = (__bf16)(w.o[ob][4 * g4 + 1] * inv);
+        p23[0] = (__bf16)(w.o[ob][4 * g4 + 2] * inv);
+        p23[1] = (__bf16)(w.o[ob][4 * g4 + 3] * inv);
         uint2 pk;
         pk.x = __builtin_bit_cast(unsigned, p01);
         pk.y = __builtin_bit_cast(unsigned, p23);
         *reinterpret_cast<uint2*>(op + d) = pk;
       }
     if (a.lse != nullptr && half == 0)
-      a.lse[((int64_t)b * a.heads + h) * a.q_stride + qrow] = (m_ref + __log2f(l_tot)) * kLn2;
+      a.lse[((int64_t)b * a.heads + h) * a.q_stride + qrow] = (w.m_ref + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -437,15 +509,15 @@ __global__ __launch_bounds__(kF32QTile) void attention_f32_kernel(const AttnArgs
 
 }  // namespace
 
-int attention_bf16_q_tile() { return kQTile; }
+int attention_bf16_q_tile(int head_dim) { return head_dim == 64 ? Tile<64>::QTILE : Tile<128>::QTILE; }
 int attention_f32_q_tile() { return kF32QTile; }
 
 hipError_t launch_attention_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
   const dim3 grid(8 * a.tasks_per_xcd);
   if (head_dim == 64)
-    hipLaunchKernelGGL(attention_bf16_kernel<64>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attention_bf16_kernel<64>, grid, dim3(Tile<64>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(attention_bf16_kernel<128>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attention_bf16_kernel<128>, grid, dim3(Tile<128>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ struct AttnArgs {
 };
 hipError_t launch_attention_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_attention_f32(const AttnArgs& a, int head_dim, hipStream_t s);
-int attention_bf16_q_tile();   // queries per workgroup of the bf16 kernel
+int attention_bf16_q_tile(int head_dim);   // queries per workgroup of the bf16 kernel
 int attention_f32_q_tile();
 
 // ---- block update -----------------------------------------------------------
