@@ -60,7 +60,9 @@ _SIGS = {
     "ba_cache_append": (_I32, [ctypes.POINTER(ba_ring), _P, _P, _I32, ctypes.POINTER(_I32), _P]),
     "ba_cache_append_batched": (_I32, [ctypes.POINTER(ba_ring), _P, _P, _I32, ctypes.POINTER(_I32), _I32, _P]),
     "ba_block_attention": (_I32, [_P, _I32, ctypes.POINTER(ba_ring), ctypes.POINTER(ba_ring),
-                                  ctypes.POINTER(ba_block_meta), _I32, ctypes.c_float, _P, _P, _P]),
+                                  ctypes.POINTER(ba_block_meta), _I32, ctypes.c_float, _P, _P,
+                                  _P, ctypes.c_size_t, _P]),
+    "ba_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
     "ba_block_update": (_I32, [_P, _P, _I64, ctypes.POINTER(_I32), _I32, ctypes.POINTER(ba_schedule), _P]),
     "ba_schedule_coefficients": (_I32, [ctypes.POINTER(ba_schedule), ctypes.POINTER(_I32), _I32,
                                         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
@@ -204,11 +206,34 @@ def make_meta(q_len, segs, text_slot=0, text_len=0):
     return m
 
 
-def ba_block_attention(q, cache, text, metas, scale=0.0, out=None, lse=None):
+def ba_attention_workspace_bytes(head_dim, dtype, n_blocks, q_stride, heads):
+    return _lib.ba_attention_workspace_bytes(head_dim, dtype, n_blocks, q_stride, heads)
+
+
+_WORKSPACES = {}
+
+
+def attention_workspace(head_dim, dtype, n_blocks, q_stride, heads, device=None):
+    """A workspace for ba_block_attention, cached per device and size.  Calls
+    that share it must be ordered on one stream.  None when none is used."""
+    nbytes = ba_attention_workspace_bytes(head_dim, dtype, n_blocks, q_stride, heads)
+    if nbytes == 0:
+        return None
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    key = (dev, nbytes)
+    ws = _WORKSPACES.get(key)
+    if ws is None:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+        _WORKSPACES[key] = ws
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + nbytes]
+
+
+def ba_block_attention(q, cache, text, metas, scale=0.0, out=None, lse=None, workspace="auto"):
     """q: [n_blocks][q_stride][heads][head_dim]; metas: list of ba_block_meta
     or dicts (q_len, segs, text_slot, text_len).  Returns out (allocated if
-    not given); lse, when given, is filled in."""
-
+    not given); lse, when given, is filled in.  workspace: "auto" (a cached
+    one), None (one workgroup per query tile), or a uint8 device tensor."""
     nb, q_stride = q.shape[0], q.shape[1]
     if q.shape[2] != cache.desc.heads or q.shape[3] != cache.desc.head_dim:
         raise ValueError("q shape does not match the cache ring")
@@ -224,10 +249,17 @@ def ba_block_attention(q, cache, text, metas, scale=0.0, out=None, lse=None):
         raise ValueError("out must match q")
     if lse is not None and (lse.dtype != torch.float32 or lse.numel() < nb * cache.desc.heads * q_stride):
         raise ValueError("lse must be fp32 [n_blocks][heads][q_stride]")
+    if isinstance(workspace, str) and workspace == "auto":
+        workspace = attention_workspace(cache.desc.head_dim, cache.desc.dtype, nb, q_stride,
+                                        cache.desc.heads, q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     _check(_lib.ba_block_attention(_dev(q, "q"), q_stride, ctypes.byref(cache.desc),
                                    ctypes.byref(text.desc) if text is not None else None,
                                    arr, nb, float(scale), _dev(out, "out"),
-                                   _dev(lse, "lse") if lse is not None else None, _stream()),
+                                   _dev(lse, "lse") if lse is not None else None,
+                                   ws_ptr, ws_bytes, _stream()),
            "ba_block_attention")
     return out
 

@@ -105,6 +105,16 @@ void coefficients(const std::vector<double>& ab, int stride, int t, float* c1, f
   *c2 = (float)(sqrt(1.0 - ap) - sqrt(ap) * sqrt(1.0 - at) / sqrt(at));
 }
 
+// Workgroups of the bf16 attention kernel the current device holds at once.
+hipError_t resident_workgroups(int head_dim, int* n) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = ba::attention_bf16_resident(head_dim, &per_cu);
+  *n = e == hipSuccess ? cus * per_cu : 0;
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,9 +219,19 @@ ba_status ba_cache_append_batched(const ba_ring* ring, const void* k, const void
   return append_common(ring, k, v, n_tokens, slots, n_blocks, stream);
 }
 
+size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_blocks, int32_t q_stride,
+                                    int32_t heads) {
+  if (dtype != BA_BF16 || (head_dim != 64 && head_dim != 128) || n_blocks < 1 || q_stride < 1 || heads < 1)
+    return 0;
+  int wg = 0;
+  if (resident_workgroups(head_dim, &wg) != hipSuccess || wg < 1) return 0;
+  // two partial results per tail workgroup, one tail workgroup per resident slot
+  return (size_t)2 * (wg / 8 * 8) * ba::attention_partial_bytes(head_dim);
+}
+
 ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cache, const ba_ring* text,
                              const ba_block_meta* meta, int32_t n_blocks, float scale, void* out,
-                             float* lse, hipStream_t stream) {
+                             float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   ba_status st = check_ring(cache, "cache");
   if (st != BA_OK) return st;
   if (n_blocks < 0) return fail(BA_ERR_INVALID_ARG, "n_blocks < 0");
@@ -220,6 +240,8 @@ ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cac
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(BA_ERR_INVALID_ARG, "q or out not 16-byte aligned");
   if (lse != nullptr && !aligned(lse, 4)) return fail(BA_ERR_INVALID_ARG, "lse not 4-byte aligned");
   if (q_stride < 1) return fail(BA_ERR_INVALID_ARG, "q_stride < 1");
+  if (workspace != nullptr && !aligned(workspace, 256))
+    return fail(BA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   if (!isfinite(scale)) return fail(BA_ERR_INVALID_ARG, "scale is not finite");
   bool need_text = false;
   for (int b = 0; b < n_blocks; ++b) need_text |= meta[b].text_len != 0;
@@ -278,14 +300,29 @@ ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cac
   const int qtile = bf16 ? ba::attention_bf16_q_tile(D) : ba::attention_f32_q_tile();
   const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
   const int eb = elem_bytes(cache->dtype);
+  int resident = 0;   // workgroups the device holds at once (split schedule)
+  if (bf16 && workspace != nullptr) {
+    hipError_t e = resident_workgroups(D, &resident);
+    if (e != hipSuccess) return hip_fail(e, "device query");
+  }
   for (int first = 0; first < n_blocks; first += ba::kAttnMaxBlocks) {
     const int nb = n_blocks - first < ba::kAttnMaxBlocks ? n_blocks - first : ba::kAttnMaxBlocks;
     ba::AttnArgs a;
     memset(&a, 0, sizeof(a));
     int32_t qm = 0;
+    int64_t tasks = 0, work = 0;
     for (int i = 0; i < nb; ++i) {
-      a.blk[i] = blocks[first + i];
-      if (a.blk[i].q_len > qm) qm = a.blk[i].q_len;
+      ba::AttnBlock& B = a.blk[i];
+      B = blocks[first + i];
+      if (B.q_len > qm) qm = B.q_len;
+      B.nqt = (B.q_len + qtile - 1) / qtile;
+      for (int sg = 0; sg < B.n_segs; ++sg) B.n_tiles += (B.len[sg] + ba::kKeyTile - 1) / ba::kKeyTile;
+      B.task_start = (int32_t)tasks;
+      B.work_start = (int32_t)work;
+      tasks += (int64_t)H * B.nqt;
+      work += (int64_t)H * B.nqt * B.n_tiles;
+      if (work >= ((int64_t)1 << 31) || tasks >= ((int64_t)1 << 30))
+        return fail(BA_ERR_OUT_OF_RANGE, "too much attention work in one call");
     }
     if (qm == 0) continue;
     const int64_t blk_elems = (int64_t)q_stride * H * D;
@@ -298,13 +335,37 @@ ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cac
     a.text_tpad = text ? text->slot_stride_tokens : 0;
     a.q_stride = q_stride;
     a.heads = H;
-    a.n_qtiles = (qm + qtile - 1) / qtile;
-    const int64_t total = (int64_t)nb * H * a.n_qtiles;
-    if (total > (int64_t)1 << 30) return fail(BA_ERR_OUT_OF_RANGE, "too many attention tasks");
-    a.total_tasks = (int32_t)total;
-    a.tasks_per_xcd = (a.total_tasks + 7) / 8;
+    a.n_blocks = nb;
     a.qscale = (float)((double)sc * 1.4426950408889634);
     a.scale_ln = sc;
+    // fp32 kernel: one workgroup per (block, head, query tile)
+    a.n_qtiles = (qm + qtile - 1) / qtile;
+    a.total_tasks = nb * H * a.n_qtiles;
+    a.tasks_per_xcd = (a.total_tasks + 7) / 8;
+    // bf16 kernel: one task per workgroup, or (with a workspace) equal ranges
+    // of task tiles over the workgroups the device holds at once
+    a.n_tasks = (int32_t)tasks;
+    a.total_work = (int32_t)work;
+    a.wg_per_xcd = (int32_t)((tasks + 7) / 8);   // default: one whole task per workgroup
+    if (resident > 0) {
+      const size_t pb = ba::attention_partial_bytes(D);
+      int64_t tail = resident / 8;           // tail workgroups per XCD: one per resident slot
+      const int64_t fit = (int64_t)(workspace_bytes / (16 * pb));
+      if (tail > fit) tail = fit;
+      if (tail >= 1 && tasks >= 8 * tail) {
+        a.split = 1;
+        a.tail_wg = (int32_t)tail;
+        a.partials = static_cast<float*>(workspace);
+        int whole_max = 0, tail_tasks_max = 0;
+        for (int x = 0; x < 8; ++x) {
+          const ba::XcdPlan p = ba::xcd_plan(a, x);
+          if (p.whole > whole_max) whole_max = p.whole;
+          if (p.t1 - p.t0 - p.whole > tail_tasks_max) tail_tasks_max = p.t1 - p.t0 - p.whole;
+        }
+        a.wg_per_xcd = whole_max + a.tail_wg;
+        a.merge_per_xcd = tail_tasks_max;
+      }
+    }
     hipError_t e = bf16 ? ba::launch_attention_bf16(a, D, stream) : ba::launch_attention_f32(a, D, stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
   }

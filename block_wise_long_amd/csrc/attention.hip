@@ -48,7 +48,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKTile = 64;         // keys per LDS tile
+constexpr int kKTile = kKeyTile;   // keys per LDS tile
 constexpr float kLazyThreshold = 4096.0f;   // 2^12: bound on a tile's weight sum
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -291,6 +291,90 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
   w.l_sum += l_g;
 }
 
+// Work unit = one 64-key tile of one task (block, head, query tile).
+struct Where {
+  int b;        // block
+  int ti;       // task within the block (head-major, query tile fastest)
+  int tile;     // first tile
+};
+
+__device__ __forceinline__ Where locate(const AttnArgs& a, int pos) {
+  int b = 0;
+  while (b + 1 < a.n_blocks && a.blk[b + 1].work_start <= pos) ++b;
+  const int r = pos - a.blk[b].work_start;
+  const int nt = a.blk[b].n_tiles;
+  Where w;
+  w.b = b;
+  w.ti = r / nt;
+  w.tile = r - w.ti * nt;
+  return w;
+}
+
+template <int D>
+struct Partial {
+  // [wave][o block][element][lane] accumulators, then [wave][lane] m, then l
+  static constexpr int NW = Shape<D>::NW;
+  static constexpr int O_FLOATS = NW * (D / 32) * 16 * 64;
+  static constexpr int FLOATS = O_FLOATS + 2 * NW * 64;
+};
+
+template <int D>
+__device__ __forceinline__ void store_partial(float* part, int wave, int lane, const WaveState<D>& w) {
+  constexpr int NOB = D / 32;
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part[((wave * NOB + ob) * 16 + i) * 64 + lane] = w.o[ob][i];
+  part[Partial<D>::O_FLOATS + wave * 64 + lane] = w.m_ref;
+  part[Partial<D>::O_FLOATS + Partial<D>::NW * 64 + wave * 64 + lane] = w.l_sum;
+}
+
+// w <- w merged with the partial result at `part` (same lanes, same queries).
+template <int D>
+__device__ __forceinline__ void merge_partial(const float* part, int wave, int lane, WaveState<D>& w) {
+  constexpr int NOB = D / 32;
+  const float m2 = part[Partial<D>::O_FLOATS + wave * 64 + lane];
+  const float l2 = part[Partial<D>::O_FLOATS + Partial<D>::NW * 64 + wave * 64 + lane];
+  const float m = fmaxf(w.m_ref, m2);
+  // (the state being folded into starts at m = -inf: equal maxima scale by 1)
+  const float a1 = w.m_ref == m ? 1.f : __builtin_amdgcn_exp2f(w.m_ref - m);
+  const float a2 = m2 == m ? 1.f : __builtin_amdgcn_exp2f(m2 - m);
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      w.o[ob][i] = w.o[ob][i] * a1 + part[((wave * NOB + ob) * 16 + i) * 64 + lane] * a2;
+  w.l_sum = w.l_sum * a1 + l2 * a2;
+  w.m_ref = m;
+}
+
+template <int D>
+__device__ __forceinline__ void store_output(const AttnArgs& a, int b, int h, int qrow, bool row_ok, int half,
+                                             const WaveState<D>& w) {
+  constexpr int NOB = D / 32;
+  const float l_tot = w.l_sum + exchange_half(w.l_sum);
+  const float inv = 1.0f / l_tot;
+  if (!row_ok) return;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)b * a.q_stride + qrow) * a.heads + h) * D;
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * ob + 8 * g4 + 4 * half;
+      bf16x2 p01, p23;
+      p01[0] = (__bf16)(w.o[ob][4 * g4 + 0] * inv);
+      p01[1] = (__bf16)(w.o[ob][4 * g4 + 1] * inv);
+      p23[0] = (__bf16)(w.o[ob][4 * g4 + 2] * inv);
+      p23[1] = (__bf16)(w.o[ob][4 * g4 + 3] * inv);
+      uint2 pk;
+      pk.x = __builtin_bit_cast(unsigned, p01);
+      pk.y = __builtin_bit_cast(unsigned, p23);
+      *reinterpret_cast<uint2*>(op + d) = pk;
+    }
+  if (a.lse != nullptr && half == 0)
+    a.lse[((int64_t)b * a.heads + h) * a.q_stride + qrow] = (w.m_ref + __log2f(l_tot)) * kLn2;
+}
+
 template <int D>
 __global__ __launch_bounds__(Tile<D>::THREADS)
 __attribute__((amdgpu_waves_per_eu(Shape<D>::WAVES_PER_SIMD, Shape<D>::WAVES_PER_SIMD)))
@@ -300,129 +384,202 @@ void attention_bf16_kernel(const AttnArgs a) {
   constexpr int NOB = D / 32;        // 32-row blocks of O^T
   __shared__ u32x4 lds[kBuffers][T::CH];
 
-  // ---- task (XCD-major order) ---------------------------------------------
-  const int wg = blockIdx.x;
-  const int task = (wg & 7) * a.tasks_per_xcd + (wg >> 3);
-  if (task >= a.total_tasks) return;
-  const int qt = task % a.n_qtiles;
-  const int h = (task / a.n_qtiles) % a.heads;
-  const int b = task / (a.n_qtiles * a.heads);
-  const AttnBlock& B = a.blk[b];
-  const int q0 = qt * T::QTILE;
-  if (q0 >= B.q_len) return;
+  // ---- this workgroup's work ------------------------------------------------
+  // The hardware deals workgroups round-robin to the 8 XCDs (workgroup w runs
+  // on XCD w % 8).  Tasks are dealt so that each XCD works through its own
+  // contiguous stretch of tasks (same block and head, neighbouring query
+  // tiles, hence the same K/V stream in its L2), and a cut task is shared only
+  // by workgroups of one XCD.
+  const int wgid = blockIdx.x;
+  const int x = wgid & 7;
+  const int j_wg = wgid >> 3;                // place in the XCD's list
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int wave = tid >> 6;
-  const int qrow = q0 + wave * 32 + (lane & 31);
-  const bool row_ok = qrow < B.q_len;
-  const int qrow_c = row_ok ? qrow : B.q_len - 1;
-  const bool active = q0 + wave * 32 < B.q_len;      // wave has queries (uniform)
-
-  // ---- Q fragment: B operand of S^T = K Q^T, exactly as given ---------------
-  bf16x8 qf[NKS];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (((int64_t)b * a.q_stride + qrow_c) * a.heads + h) * D;
-#pragma unroll
-    for (int s = 0; s < NKS; ++s)
-      qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * half));
-  }
   const float c = a.qscale;
 
-  // ---- key tiles: 64 keys each, two 32-key groups ---------------------------
-  int n_tiles = 0;
-  for (int sg = 0; sg < B.n_segs; ++sg) n_tiles += (B.len[sg] + kKTile - 1) / kKTile;
-
-  Cursor lc;                                  // cursor of the last tile loaded
-  lc.seg = 0;
-  open_segment<D>(a, B, h, lc);
-  Cursor cc = lc;                             // cursor of the tile being consumed
-  load_tile<D>(lc, tid, lds[0]);
-  if (n_tiles > 1) {
-    advance<D>(a, B, h, lc);
-    load_tile<D>(lc, tid, lds[1]);
+  // one range of work: a whole task, or (split) a share of the XCD's tail
+  XcdPlan plan;
+  int pos, end;
+  bool first_chunk = true;                    // first chunk of the range
+  int tail_j = 0;                             // tail workgroup index within the XCD
+  if (!a.split) {
+    const int t = x * a.wg_per_xcd + j_wg;
+    if (t >= a.n_tasks) return;
+    pos = task_work_start(a, t);
+    end = pos + a.blk[locate(a, pos).b].n_tiles;
+  } else {
+    plan = xcd_plan(a, x);
+    if (j_wg < plan.whole) {
+      pos = task_work_start(a, plan.t0 + j_wg);
+      end = pos + a.blk[locate(a, pos).b].n_tiles;
+    } else {
+      tail_j = j_wg - plan.whole;
+      const int n = plan.tail1 - plan.tail0;
+      if (tail_j >= a.tail_wg || n <= 0) return;
+      pos = plan.tail0 + split_start(n, a.tail_wg, tail_j);
+      end = plan.tail0 + split_start(n, a.tail_wg, tail_j + 1);
+    }
   }
 
-  {
-    // buffer 2 starts as zeros: the first step's deferred PV reads it
-    const u32x4 z = {0u, 0u, 0u, 0u};
+  while (pos < end) {
+    // ---- the chunk: tiles [tile0, tile0 + n_tiles) of one task ----------
+    const Where at = locate(a, pos);
+    const AttnBlock& B = a.blk[at.b];
+    const int b = at.b;
+    const int h = at.ti / B.nqt;
+    const int qt = at.ti - h * B.nqt;
+    const int tile0 = at.tile;
+    const int left = end - pos;
+    const int n_tiles = B.n_tiles - tile0 < left ? B.n_tiles - tile0 : left;
+    const bool whole = tile0 == 0 && n_tiles == B.n_tiles;
+
+    const int q0 = qt * T::QTILE;
+    const int qrow = q0 + wave * 32 + (lane & 31);
+    const bool row_ok = qrow < B.q_len;
+    const int qrow_c = row_ok ? qrow : B.q_len - 1;
+    const bool active = q0 + wave * 32 < B.q_len;    // wave has queries (uniform)
+
+    // Q fragment: B operand of S^T = K Q^T, exactly as given
+    bf16x8 qf[NKS];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                           (((int64_t)b * a.q_stride + qrow_c) * a.heads + h) * D;
 #pragma unroll
-    for (int u = 0; u < T::LOADS; ++u) lds[2][u * T::THREADS + tid] = z;
+      for (int s = 0; s < NKS; ++s)
+        qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * half));
+    }
+
+    // cursor at tile0: skip whole segments, then the tiles before it
+    Cursor lc;
+    {
+      int rem = tile0;
+      int sg = 0;
+      for (; sg + 1 < B.n_segs; ++sg) {
+        const int nt = (B.len[sg] + kKTile - 1) / kKTile;
+        if (rem < nt) break;
+        rem -= nt;
+      }
+      lc.seg = sg;
+      open_segment<D>(a, B, h, lc);
+      lc.off = rem * kKTile;
+    }
+    Cursor cc = lc;                           // cursor of the tile being consumed
+    load_tile<D>(lc, tid, lds[0]);
+    if (n_tiles > 1) {
+      advance<D>(a, B, h, lc);
+      load_tile<D>(lc, tid, lds[1]);
+    }
+    {
+      // buffer 2 starts as zeros: the first step's deferred PV reads it
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < T::LOADS; ++u) lds[2][u * T::THREADS + tid] = z;
+    }
+    WaveState<D> w;
+#pragma unroll
+    for (int j = 0; j < NOB; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w.o[j][i] = 0.f;
+    w.m_ref = 0.f;
+    w.l_sum = 0.f;
+    wait_loads();
+    __syncthreads();
+
+    // Software pipeline over 32-key groups (two per tile).  Tile t lives in
+    // buffer t % 3; tile t+2 starts loading when tile t+1 is published, after
+    // every wave has issued its last read of the buffer it overwrites.  Every
+    // step has the same shape: the first step's deferred PV multiplies zero
+    // weights with the zero-filled third buffer, and the last step's look-ahead
+    // QK^T reads whatever the next buffer holds and is discarded.
+    f32x16 sa, sb;                            // raw scores of even / odd groups
+    bf16x8 p[2];                              // weights of the previous group
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[k2][i] = (__bf16)0.0f;
+    if (active) sa = scores<D>(lds[0], lane, 0, qf);
+    int buf = 0;                              // buffer of the current tile
+    for (int t = 0; t < n_tiles; ++t) {
+      const int nbuf = buf == 2 ? 0 : buf + 1;
+      const int pbuf = buf == 0 ? 2 : buf - 1;
+      const int valid = cc.len - cc.off;
+      // group 2t: S of group 2t+1 (same tile), PV of group 2t-1 (previous tile)
+      if (active)
+        pipe_step<D>(lds[buf], 1, lds[pbuf], 1, lane, qf, c, sa, sb, p, valid, t == 0, w);
+      if (t + 1 < n_tiles) {
+        // publish tile t+1, start loading tile t+2 into the buffer of tile t-1
+        wait_loads();
+        __syncthreads();
+        if (t + 2 < n_tiles) {
+          advance<D>(a, B, h, lc);
+          load_tile<D>(lc, tid, lds[pbuf]);
+        }
+        advance<D>(a, B, h, cc);
+      }
+      // group 2t+1: S of group 2t+2 (next tile), PV of group 2t (this tile)
+      if (active)
+        pipe_step<D>(lds[nbuf], 0, lds[buf], 0, lane, qf, c, sb, sa, p, valid - 32, false, w);
+      buf = nbuf;
+    }
+    if (active) accumulate<D>(lds[buf == 0 ? 2 : buf - 1], lane, 1, p, w.o);
+
+    if (whole) {
+      store_output<D>(a, b, h, qrow, row_ok, half, w);
+    } else {
+      // a cut task: the merge kernel combines the pieces after this launch
+      store_partial<D>(a.partials + ((int64_t)2 * (x * a.tail_wg + tail_j) + (first_chunk ? 0 : 1)) *
+                                        Partial<D>::FLOATS, wave, lane, w);
+    }
+    pos += n_tiles;
+    first_chunk = false;
+    __syncthreads();                          // LDS buffers are reused by the next chunk
   }
+}
+
+
+// Second pass of the split schedule: every tail task that the tail
+// workgroups cut is folded from its pieces (in workgroup order, so the result
+// does not depend on timing) and normalised.  Same wave/lane layout as the
+// main kernel, so each lane reads back exactly what it wrote.
+template <int D>
+__global__ __launch_bounds__(Tile<D>::THREADS) void attention_merge_kernel(const AttnArgs a) {
+  constexpr int NOB = D / 32;
+  const int x = blockIdx.x & 7;
+  const int u = blockIdx.x >> 3;
+  const XcdPlan plan = xcd_plan(a, x);
+  const int t = plan.t0 + plan.whole + u;
+  if (t >= plan.t1) return;
+  const int tstart = task_work_start(a, t);
+  const Where at = locate(a, tstart);
+  const AttnBlock& B = a.blk[at.b];
+  const int n_tail = plan.tail1 - plan.tail0;
+  const int j_lo = split_owner(n_tail, a.tail_wg, tstart - plan.tail0);
+  const int j_hi = split_owner(n_tail, a.tail_wg, tstart + B.n_tiles - 1 - plan.tail0);
+  if (j_lo == j_hi) return;                  // ran whole inside one tail range
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int wave = tid >> 6;
+  const int h = at.ti / B.nqt;
+  const int qt = at.ti - h * B.nqt;
+  const int qrow = qt * Tile<D>::QTILE + wave * 32 + (lane & 31);
   WaveState<D> w;
 #pragma unroll
   for (int j = 0; j < NOB; ++j)
 #pragma unroll
     for (int i = 0; i < 16; ++i) w.o[j][i] = 0.f;
-  w.m_ref = 0.f;
+  w.m_ref = -INFINITY;
   w.l_sum = 0.f;
-  wait_loads();
-  __syncthreads();
-
-  // Software pipeline over 32-key groups (two per tile).  Tile t lives in
-  // buffer t % 3; tile t+2 starts loading when tile t+1 is published, after
-  // every wave has issued its last read of the buffer it overwrites.  Every
-  // step has the same shape: the first step's deferred PV multiplies zero
-  // weights with the zero-filled third buffer, and the last step's look-ahead
-  // QK^T reads whatever the next buffer holds and is discarded.
-  f32x16 sa, sb;                              // raw scores of even / odd groups
-  bf16x8 p[2];                                // weights of the previous group
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[k2][i] = (__bf16)0.0f;
-  if (active) sa = scores<D>(lds[0], lane, 0, qf);
-  int buf = 0;                                // buffer of the current tile
-  for (int t = 0; t < n_tiles; ++t) {
-    const int nbuf = buf == 2 ? 0 : buf + 1;
-    const int pbuf = buf == 0 ? 2 : buf - 1;
-    const int valid = cc.len - cc.off;
-    // group 2t: S of group 2t+1 (same tile), PV of group 2t-1 (previous tile)
-    if (active)
-      pipe_step<D>(lds[buf], 1, lds[pbuf], 1, lane, qf, c, sa, sb, p, valid, t == 0, w);
-    if (t + 1 < n_tiles) {
-      // publish tile t+1, start loading tile t+2 into the buffer of tile t-1
-      wait_loads();
-      __syncthreads();
-      if (t + 2 < n_tiles) {
-        advance<D>(a, B, h, lc);
-        load_tile<D>(lc, tid, lds[pbuf]);
-      }
-      advance<D>(a, B, h, cc);
-    }
-    // group 2t+1: S of group 2t+2 (next tile), PV of group 2t (this tile)
-    if (active)
-      pipe_step<D>(lds[nbuf], 0, lds[buf], 0, lane, qf, c, sb, sa, p, valid - 32, false, w);
-    buf = nbuf;
+  for (int oj = j_lo; oj <= j_hi; ++oj) {
+    // the task opens tail workgroup oj's range (slot 0) or follows its first chunk (slot 1)
+    const int slot = plan.tail0 + split_start(n_tail, a.tail_wg, oj) >= tstart ? 0 : 1;
+    merge_partial<D>(a.partials + ((int64_t)2 * (x * a.tail_wg + oj) + slot) * Partial<D>::FLOATS, wave,
+                     lane, w);
   }
-  if (active) accumulate<D>(lds[buf == 0 ? 2 : buf - 1], lane, 1, p, w.o);
-
-  // ---- epilogue: normalise, round to bf16, store --------------------------
-  const float l_tot = w.l_sum + exchange_half(w.l_sum);
-  const float inv = 1.0f / l_tot;
-  if (row_ok) {
-    uint16_t* op = static_cast<uint16_t*>(a.out) +
-                   (((int64_t)b * a.q_stride + qrow) * a.heads + h) * D;
-#pragma unroll
-    for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * ob + 8 * g4 + 4 * half;
-        bf16x2 p01, p23;
-        p01[0] = (__bf16)(w.o[ob][4 * g4 + 0] * inv);
-        p01[1] = (__bf16)(w.o[ob][4 * g4 + 1] * inv);
-        p23[0] = (__bf16)(w.o[ob][4 * g4 + 2] * inv);
-        p23[1] = (__bf16)(w.o[ob][4 * g4 + 3] * inv);
-        uint2 pk;
-        pk.x = __builtin_bit_cast(unsigned, p01);
-        pk.y = __builtin_bit_cast(unsigned, p23);
-        *reinterpret_cast<uint2*>(op + d) = pk;
-      }
-    if (a.lse != nullptr && half == 0)
-      a.lse[((int64_t)b * a.heads + h) * a.q_stride + qrow] = (w.m_ref + __log2f(l_tot)) * kLn2;
-  }
+  store_output<D>(a, at.b, h, qrow, qrow < B.q_len, half, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -511,13 +668,30 @@ __global__ __launch_bounds__(kF32QTile) void attention_f32_kernel(const AttnArgs
 
 int attention_bf16_q_tile(int head_dim) { return head_dim == 64 ? Tile<64>::QTILE : Tile<128>::QTILE; }
 int attention_f32_q_tile() { return kF32QTile; }
+int attention_bf16_threads(int head_dim) { return head_dim == 64 ? Tile<64>::THREADS : Tile<128>::THREADS; }
+size_t attention_partial_bytes(int head_dim) {
+  return sizeof(float) * (head_dim == 64 ? Partial<64>::FLOATS : Partial<128>::FLOATS);
+}
+
+hipError_t attention_bf16_resident(int head_dim, int* per_cu) {
+  if (head_dim == 64)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<64>, Tile<64>::THREADS, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<128>, Tile<128>::THREADS, 0);
+}
 
 hipError_t launch_attention_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid(8 * a.tasks_per_xcd);
+  const dim3 grid(8 * a.wg_per_xcd);
   if (head_dim == 64)
     hipLaunchKernelGGL(attention_bf16_kernel<64>, grid, dim3(Tile<64>::THREADS), 0, s, a);
   else
     hipLaunchKernelGGL(attention_bf16_kernel<128>, grid, dim3(Tile<128>::THREADS), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.split || a.merge_per_xcd == 0) return e;
+  const dim3 mgrid(8 * a.merge_per_xcd);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(attention_merge_kernel<64>, mgrid, dim3(Tile<64>::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(attention_merge_kernel<128>, mgrid, dim3(Tile<128>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

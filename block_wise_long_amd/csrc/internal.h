@@ -8,6 +8,7 @@
 namespace ba {
 
 constexpr int kTokenAlign = 64;          // ring slot stride granularity
+constexpr int kKeyTile = 64;             // keys per attention tile (divides kTokenAlign)
 constexpr int kAppendMaxBlocks = 64;     // slots per append launch (kernarg)
 constexpr int kAttnMaxBlocks = 16;       // blocks per attention launch (kernarg)
 constexpr int kAttnMaxSegs = 9;          // 8 cache segments + text
@@ -35,6 +36,10 @@ struct AttnBlock {
   int32_t n_segs;
   int32_t slot[kAttnMaxSegs];
   int32_t len[kAttnMaxSegs];
+  int32_t n_tiles;          // 64-key tiles of the key set (sum over segments)
+  int32_t nqt;              // query tiles of this block (bf16 kernel)
+  int32_t task_start;       // first task id of this block in the launch
+  int32_t work_start;       // first work unit (task tile) of this block
 };
 
 struct AttnArgs {
@@ -52,11 +57,70 @@ struct AttnArgs {
   int32_t tasks_per_xcd;    // ceil(total_tasks / 8)
   float qscale;             // scale * log2(e)
   float scale_ln;           // scale (fp32 kernel), ln(2) factor for lse
+  // bf16 kernel schedule; XCD x (workgroup w runs on XCD w % 8) owns tasks
+  // [x*n_tasks/8, (x+1)*n_tasks/8) and takes them in order.  split = 0: one
+  // whole task per workgroup.  split = 1: the XCD's tasks but about its last
+  // round run as whole-task workgroups; the rest of its task tiles is shared
+  // evenly by tail_wg tail workgroups, which write the partial results of the
+  // tasks they cut to the workspace; a second kernel merges them.
+  float* partials;          // [8 * tail_wg][2][partial floats] (split)
+  int32_t total_work;       // task tiles of the launch, < 2^31
+  int32_t n_tasks;
+  int32_t wg_per_xcd;       // list length per XCD
+  int32_t tail_wg;          // tail workgroups per XCD (split)
+  int32_t split;
+  int32_t n_blocks;
+  int32_t merge_per_xcd;    // merge workgroups per XCD (split)
+  int32_t pad_;
   AttnBlock blk[kAttnMaxBlocks];
 };
 hipError_t launch_attention_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
+
+// ---- split schedule (shared by host and device) ------------------------------
+// Even split of n units over k takers: taker j starts at split_start(n, k, j).
+__host__ __device__ inline int split_start(int n, int k, int j) {
+  const int q = n / k, r = n - (n / k) * k;
+  return j * q + (j < r ? j : r);
+}
+// Taker whose share holds unit u (u < n).
+__host__ __device__ inline int split_owner(int n, int k, int u) {
+  const int q = n / k, r = n - (n / k) * k;
+  const int big = r * (q + 1);
+  return u < big ? u / (q + 1) : r + (u - big) / q;
+}
+// First work unit (task tile) of task t; t = n_tasks gives the total.
+__host__ __device__ inline int task_work_start(const AttnArgs& a, int t) {
+  if (t >= a.n_tasks) return a.total_work;
+  int b = 0;
+  while (b + 1 < a.n_blocks && a.blk[b + 1].task_start <= t) ++b;
+  return a.blk[b].work_start + (t - a.blk[b].task_start) * a.blk[b].n_tiles;
+}
+// The task list of XCD x under the split schedule.
+struct XcdPlan {
+  int t0, t1;          // tasks [t0, t1)
+  int whole;           // tasks t0 .. t0 + whole - 1 run whole
+  int tail0, tail1;    // work units shared by the tail workgroups
+};
+__host__ __device__ inline XcdPlan xcd_plan(const AttnArgs& a, int x) {
+  XcdPlan p;
+  p.t0 = (int)(((int64_t)x * a.n_tasks) >> 3);
+  p.t1 = (int)(((int64_t)(x + 1) * a.n_tasks) >> 3);
+  const int wpx = a.tail_wg;               // resident workgroups of the XCD
+  const int n = p.t1 - p.t0;
+  int rounds = n / wpx;
+  // the tail takes the part of the last round that does not fill the XCD; a
+  // small one takes a whole round more, so no task is cut into many pieces
+  if ((n - rounds * wpx) * 4 < wpx && rounds > 0) --rounds;
+  p.whole = rounds * wpx;
+  p.tail0 = task_work_start(a, p.t0 + p.whole);
+  p.tail1 = task_work_start(a, p.t1);
+  return p;
+}
 hipError_t launch_attention_f32(const AttnArgs& a, int head_dim, hipStream_t s);
 int attention_bf16_q_tile(int head_dim);   // queries per workgroup of the bf16 kernel
+int attention_bf16_threads(int head_dim);  // threads per workgroup of the bf16 kernel
+size_t attention_partial_bytes(int head_dim);   // workspace bytes of one partial result
+hipError_t attention_bf16_resident(int head_dim, int* per_cu);   // workgroups per CU
 int attention_f32_q_tile();
 
 // ---- block update -----------------------------------------------------------

@@ -147,14 +147,31 @@ typedef struct {
  * scale:   > 0, or <= 0 for 1/sqrt(head_dim).
  * lse:     optional [n_blocks][heads][q_stride] fp32 log-sum-exp (natural
  *          log) of the scaled scores per query, or NULL.
+ * workspace: optional device buffer (256-byte aligned) of workspace_bytes,
+ *          see ba_attention_workspace_bytes (bf16 only).  With it, the tasks
+ *          that would form a last, partly filled wave of workgroups are split
+ *          evenly over the workgroups the device holds at once; the pieces of
+ *          a cut task are written there and folded by a second kernel on the
+ *          same stream.  Without it (NULL) each query tile is one workgroup.
+ *          Results agree to rounding either way and are deterministic.  Its
+ *          contents need no initialisation; calls that share a workspace must
+ *          be ordered on one stream.
  * bf16: products of bf16 inputs accumulate in fp32; the normalised weights
  * are rounded to bf16 for the second product and the output to bf16 (nearest
- * even).  fp32: all arithmetic in fp32.
+ * even).  fp32: all arithmetic in fp32 (the workspace is not used).
  */
 ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cache,
                              const ba_ring* text, const ba_block_meta* meta,
                              int32_t n_blocks, float scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* Workspace bytes for ba_block_attention on the current device (0: none is
+ * used, e.g. fp32, or no device): two partial results per workgroup the
+ * device holds at once.  A smaller buffer still works, with fewer workgroups
+ * sharing the split. */
+size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_blocks,
+                                    int32_t q_stride, int32_t heads);
 
 /*
  * Noise schedule of the per-block update.  NULL selects the default

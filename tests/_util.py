@@ -108,7 +108,7 @@ class Workload:
         self.B.ba_cache_append(self.text, to_dev(k, self.dtype), to_dev(v, self.dtype), k.shape[0])
         self.otext.append(k, v, k.shape[0])
 
-    def run(self, q, metas, scale=0.0, with_lse=True):
+    def run(self, q, metas, scale=0.0, with_lse=True, workspace="auto"):
         import torch
         qd = to_dev(q, self.dtype)
         lse = None
@@ -116,7 +116,8 @@ class Workload:
             lse = torch.full((q.shape[0], q.shape[2], q.shape[1]), float("nan"),
                              dtype=torch.float32, device="cuda")
         out = torch.full_like(qd, float("nan"))
-        self.B.ba_block_attention(qd, self.ring, self.text, metas, scale, out=out, lse=lse)
+        self.B.ba_block_attention(qd, self.ring, self.text, metas, scale, out=out, lse=lse,
+                                  workspace=workspace)
         torch.cuda.synchronize()
         return out, lse
 

@@ -20,7 +20,7 @@ FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dere
 
 def test_exports_every_declared_symbol():
     names = B.header_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -122,11 +122,11 @@ def _meta(q_len=10, segs=((0, 50),), text_slot=0, text_len=0):
     return B.make_meta(q_len, list(segs), text_slot, text_len)
 
 
-def _attn(cache, text, metas, q=FAKE, out=FAKE, q_stride=16, scale=0.0, lse=None):
+def _attn(cache, text, metas, q=FAKE, out=FAKE, q_stride=16, scale=0.0, lse=None, ws=None, ws_bytes=0):
     arr = (B.ba_block_meta * len(metas))(*metas)
     return B.raw.ba_block_attention(q, q_stride, ctypes.byref(cache) if cache is not None else None,
                                     ctypes.byref(text) if text is not None else None,
-                                    arr, len(metas), scale, out, lse, None)
+                                    arr, len(metas), scale, out, lse, ws, ws_bytes, None)
 
 
 def test_attention_rejects():
@@ -149,6 +149,15 @@ def test_attention_rejects():
     c2 = _ring(head_dim=96)
     assert _attn(c2, None, [_meta()]) == B.BA_ERR_UNSUPPORTED
     assert "head_dim" in B.ba_last_error()
+    assert _attn(c, None, [_meta()], ws=FAKE + 64, ws_bytes=1 << 20) == B.BA_ERR_INVALID_ARG
+    assert "workspace" in B.ba_last_error()
+
+
+def test_workspace_bytes_without_device():
+    # fp32 never uses one; with no device to size the grid, none is asked for
+    assert B.ba_attention_workspace_bytes(64, B.BA_F32, 1, 128, 2) == 0
+    assert B.ba_attention_workspace_bytes(96, B.BA_BF16, 1, 128, 2) == 0
+    assert B.ba_attention_workspace_bytes(64, B.BA_BF16, 0, 128, 2) == 0
 
 
 def test_update_rejects():

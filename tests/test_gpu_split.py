@@ -1,0 +1,80 @@
+"""The two work schedules of the bf16 attention kernel through the C ABI:
+one workgroup per query tile (no workspace) and equal ranges of key tiles
+over the resident workgroups with cut tasks merged through the workspace.
+Both must meet the bar against the oracle; the split schedule must also be
+deterministic, whatever the workspace held before."""
+import numpy as np
+import pytest
+
+from _util import Workload, check_contract, decode, to_dev, to_host_bits
+from workloads import draw
+
+pytestmark = pytest.mark.gpu
+
+
+def _rng(s):
+    return np.random.Generator(np.random.PCG64(s))
+
+
+def _setup(D, seed):
+    rng = _rng(seed)
+    H = 3
+    w = Workload("bf16", 6, 700, H, D, 120)
+    for n in (700, 650, 700, 33, 700, 699):
+        w.append(draw(rng, (n, H, D), 0.5, "bf16"), draw(rng, (n, H, D), 0.5, "bf16"))
+    w.set_text(draw(rng, (120, H, D), 0.5, "bf16"), draw(rng, (120, H, D), 0.5, "bf16"))
+    q = draw(rng, (4, 600, H, D), 0.5, "bf16")
+    metas = [{"q_len": 600, "segs": [(0, 700), (1, 650)], "text_slot": 0, "text_len": 120},
+             {"q_len": 257, "segs": [(2, 700)], "text_slot": 0, "text_len": 0},
+             {"q_len": 0, "segs": [(3, 33)], "text_slot": 0, "text_len": 3},
+             {"q_len": 333, "segs": [(3, 33), (4, 700), (5, 699)], "text_slot": 0, "text_len": 119}]
+    return w, q, metas
+
+
+def _workspace(D, tail_wg, fill):
+    """A workspace with room for exactly tail_wg tail workgroups per XCD,
+    pre-filled with garbage (its contents must not matter)."""
+    import torch
+    part = {64: 4 * 4 * (2 * 16 * 64 + 2 * 64), 128: 4 * 8 * (4 * 16 * 64 + 2 * 64)}[D]
+    nbytes = 16 * tail_wg * part
+    ws = torch.full((nbytes + 256,), fill, dtype=torch.uint8, device="cuda")
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + nbytes]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_both_schedules_meet_the_bar(D):
+    w, q, metas = _setup(D, 21 + D)
+    ref, ref_lse = w.oracle(q, metas)
+    outs = []
+    for ws in ("auto", None):
+        out, lse = w.run(q, metas, workspace=ws)
+        got = decode(out, "bf16")
+        check_contract(got, ref, "bf16", gate2=False)
+        assert np.nanmax(np.abs(lse.cpu().numpy() - ref_lse)) < 2e-3
+        assert np.isnan(got[1, 257:]).all() and np.isnan(got[2]).all() and np.isnan(got[3, 333:]).all()
+        outs.append(got)
+    vmax = max(np.abs(w.oring.values(s, h, 650)).max() for s in range(6) for h in range(3))
+    assert np.nanmax(np.abs(outs[0] - outs[1])) <= 2 * 2 ** -9 * vmax
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("tail_wg", [1, 2, 5])
+def test_few_tail_workgroups_cut_many_tasks(D, tail_wg):
+    # few tail workgroups: every tail range spans several tasks and blocks, and
+    # most tail tasks are cut between two or more workgroups
+    w, q, metas = _setup(D, 5 + D + tail_wg)
+    ref, _ = w.oracle(q, metas)
+    out1, _ = w.run(q, metas, workspace=_workspace(D, tail_wg, 0x7F))
+    out2, _ = w.run(q, metas, workspace=_workspace(D, tail_wg, 0xFF))
+    check_contract(decode(out1, "bf16"), ref, "bf16", gate2=False)
+    assert np.array_equal(to_host_bits(out1), to_host_bits(out2))
+
+
+def test_split_schedule_is_deterministic_at_video_shape():
+    from _util import build_config
+    from workloads import CONFIGS
+    w, inputs, metas = build_config(CONFIGS[1])
+    a, _ = w.run(inputs["q"], metas, with_lse=False)
+    b, _ = w.run(inputs["q"], metas, with_lse=False)
+    assert np.array_equal(to_host_bits(a), to_host_bits(b))
