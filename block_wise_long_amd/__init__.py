@@ -16,7 +16,9 @@ import re
 import torch  # noqa: F401  (load order matters, see above)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libblockattn.so")
+# BLOCKATTN_LIB selects another build of the library (e.g. a variant built
+# with different compile options); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("BLOCKATTN_LIB") or os.path.join(_HERE, "libblockattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "blockattn.h")
 
 if not os.path.exists(LIB_PATH):

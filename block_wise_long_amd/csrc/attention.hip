@@ -38,6 +38,8 @@
 // fp32 rings (small shapes, parity at 1e-5).
 #include <math.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ba {
@@ -51,6 +53,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kKTile = kKeyTile;   // keys per LDS tile
 constexpr float kLazyThreshold = 4096.0f;   // 2^12: bound on a tile's weight sum
 constexpr float kLn2 = 0.693147180559945309f;
+
 
 // Key of LDS K row r within its 32-row group: bits 2 and 3 swapped.  With it,
 // the 16 scores a lane holds for one 32-key group (rows 8(i/4) + 4(l/32) + i%4
@@ -91,6 +94,10 @@ __device__ __forceinline__ void open_segment(const AttnArgs& a, const AttnBlock&
   c.v = base + ((slot * 2 + 1) * a.heads + h) * mat;
   c.len = B.len[c.seg];
   c.off = 0;
+  // the segment table is read with scalar loads; finish them here so that no
+  // step starts with one in flight (the LDS reads of a step are then waited
+  // for one by one instead of all at once)
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
 }
 
 template <int D>
@@ -118,6 +125,7 @@ template <> struct Shape<64> { static constexpr int NW = 4, WAVES_PER_SIMD = 3; 
 template <> struct Shape<128> { static constexpr int NW = 8, WAVES_PER_SIMD = 2; };
 
 constexpr int kBuffers = 3;   // LDS tile buffers: in use, being consumed, being filled
+constexpr int kLdsAhead = 2;  // a step's LDS operand reads issued ahead of their MFMA
 
 template <int D>
 struct Tile {
@@ -144,13 +152,13 @@ struct Tile {
   static __device__ __forceinline__ int v_idx(int d, int c) { return K_CH + d * 8 + (c ^ row_swz128(d)); }
 };
 
-// Stream one K tile and one V^T tile straight from global memory into an LDS
-// buffer (global_load_lds_dwordx4: lane i of a wave fills the i-th 16 bytes
-// after the wave's LDS base).  The swizzle is applied by choosing which global
+// Stream one K tile and one V^T tile straight from global memory into the LDS
+// buffer at byte address buf_lds (global_load_lds_dwordx4: lane i of a wave
+// fills the i-th 16 bytes after the wave's LDS base, held in M0).  The swizzle is applied by choosing which global
 // chunk each lane fetches for its fixed LDS position.  Completion is waited
 // for with vmcnt before the barrier that publishes the buffer.
 template <int D>
-__device__ __forceinline__ void load_tile(const Cursor& c, int tid, u32x4* buf) {
+__device__ __forceinline__ void load_tile(const Cursor& c, int tid, unsigned buf_lds) {
   using T = Tile<D>;
   const uint16_t* kb = c.k + (int64_t)c.off * D;   // uniform tile bases
   const uint16_t* vb = c.v + c.off;
@@ -160,19 +168,31 @@ __device__ __forceinline__ void load_tile(const Cursor& c, int tid, u32x4* buf) 
   for (int u = 0; u < T::LOADS; ++u) {
     const int p0 = u * T::THREADS + wave_base;     // first LDS chunk of this wave
     const int p = p0 + lane;
-    const uint16_t* src;
+    const uint16_t* base;                          // uniform
+    unsigned idx;                                  // per lane, in elements
     if (u < T::K_LOADS) {
       const int r = p / T::KCH, pos = p % T::KCH;
       const int ch = D == 64 ? (pos ^ T::row_swz128(r)) : (pos ^ (r & 15));
-      src = kb + (unsigned)(key_of_row(r) * D + ch * 8);
+      base = kb;
+      idx = (unsigned)(key_of_row(r) * D + ch * 8);
     } else {
       const int pv = p - T::K_CH;
       const int d = pv / 8, pos = pv % 8;
       const int ch = pos ^ T::row_swz128(d);
-      src = vb + (unsigned)(d * c.tpad + ch * 8);
+      base = vb;
+      idx = (unsigned)(d * c.tpad + ch * 8);
     }
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(buf + p0), 16, 0, 0);
+    // LDS byte address of this wave's first chunk (wave-uniform).  The copy
+    // is an asm statement: it has no register result and lands in LDS, which
+    // is read only after the explicit vmcnt wait and barrier that publish the
+    // buffer.  Seen by the compiler as an LDS write in flight, it would make
+    // every LDS read of the steps wait for all outstanding LDS reads.
+    const unsigned lds_base = buf_lds + 16u * (unsigned)(u * T::THREADS) +
+                              16u * (unsigned)__builtin_amdgcn_readfirstlane(wave_base);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(idx * 2u), "s"(base), "s"(lds_base)
+                 : "memory", "m0");
   }
 }
 
@@ -187,8 +207,9 @@ __device__ __forceinline__ float exchange_half(float x) {
 // fix-up modifies live scores without creating a second copy at the join.
 // (Only VALU results are touched this way: a value an MFMA writes needs the
 // compiler's hazard tracking, so the accumulators are scaled in plain code.)
-__device__ __forceinline__ float mask_inplace(float x, bool keep) {
-  asm volatile("v_cndmask_b32 %0, %1, %0, %2" : "+v"(x) : "v"(-INFINITY), "s"(__builtin_amdgcn_ballot_w64(keep)));
+// `keep` is a wave-uniform lane mask (bit l: lane l keeps its value).
+__device__ __forceinline__ float mask_inplace(float x, uint64_t keep) {
+  asm volatile("v_cndmask_b32 %0, %1, %0, %2" : "+v"(x) : "v"(-INFINITY), "s"(keep));
   return x;
 }
 
@@ -247,30 +268,90 @@ __device__ __forceinline__ float weights(const f32x16& s, float shift, bf16x8 (&
 }
 
 // One pipeline step for group k: the matrix cores take S^T of group k+1 and
-// O^T += V^T P^T of group k-1 while the vector ALUs turn
-// the raw scores of group k into weights.  P of group k replaces p on exit.
-// `valid` counts the group's keys that lie before its segment's end (>= 32:
-// all); keys past it get weight 0 in a fix-up that only tail groups run, so
-// the common path carries no mask.
+// O^T += V^T P^T of group k-1 while the vector ALUs turn the raw scores of
+// group k into weights.  P of group k replaces p on exit.  `valid` counts the
+// group's keys that lie before its segment's end (>= 32: all); the others get
+// score -inf in a fix-up that only tail groups run, ahead of the hot block.
 template <int D>
 __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* Lp, int gp, int lane,
                                           const bf16x8 (&qf)[D / 16], float c, const f32x16& s_in,
                                           f32x16& s_out, bf16x8 (&p)[2], int valid, bool first,
                                           WaveState<D>& w) {
   constexpr int NOB = D / 32;
-  s_out = scores<D>(Ls, lane, gs, qf);
-  accumulate<D>(Lp, lane, gp, p, w.o);
   f32x16 sc;
   const float mneg = -w.m_ref;
 #pragma unroll
   for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(s_in[i], c, mneg);
-  float l_g = weights(sc, 0.f, p);
   if (__builtin_expect(valid < 32, 0)) {
-    // tail group: element i is key 16(i/8) + 8*half + i%8 of the group
-    const int lim = valid - 8 * (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = mask_inplace(sc[i], 16 * (i >> 3) + (i & 7) < lim);
-    l_g = weights(sc, 0.f, p);
+    for (int i = 0; i < 16; ++i) {
+      // key of element i: 16(i/8) + i%8 in lanes 0-31, 8 more in lanes 32-63
+      const int key = 16 * (i >> 3) + (i & 7);
+      const uint64_t keep = (key < valid ? 0xFFFFFFFFull : 0ull) | (key + 8 < valid ? ~0xFFFFFFFFull : 0ull);
+      sc[i] = mask_inplace(sc[i], keep);
+    }
+  }
+  // ---- hot block: matrix cores and vector ALUs work side by side ----------
+  // The wave issues in order, so the step is laid out by hand: each MFMA is
+  // followed by the LDS read of the operand two MFMAs ahead and by its share
+  // of the weight computation (one of eight chunks after every MFMA at
+  // D = 64, after every second one at D = 128); scheduling barriers keep the
+  // compiler from regrouping them.
+  float l_g;
+  {
+    // nothing of the LGKM counter is outstanding here: with that known, each
+    // MFMA below waits only for its own operand
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    using T = Tile<D>;
+    constexpr int NKS = D / 16;
+    constexpr int NM = NKS + 2 * NOB;           // MFMAs of the step
+    constexpr int LA = kLdsAhead;               // LDS reads in flight ahead of use
+    const int half = lane >> 5;
+    const int r = 32 * gs + (lane & 31);
+    // MFMA slot m: QK^T k-step m/2 on even slots while those last, PV
+    // products (k2, ob) on the others: two independent accumulator chains
+    auto is_qk = [](int m) { return m < 2 * NKS && (m & 1) == 0; };
+    auto pv_of = [](int m) { return m < 2 * NKS ? m / 2 : m - NKS; };
+    auto operand = [&](int m) {
+      if (is_qk(m)) return as_bf16x8(Ls[T::k_idx(r, 2 * (m / 2) + half)]);
+      const int pv = pv_of(m), k2 = pv / NOB, ob = pv % NOB;
+      return as_bf16x8(Lp[T::v_idx(32 * ob + (lane & 31), 4 * gp + 2 * k2 + half)]);
+    };
+    bf16x8 fr[NM];
+#pragma unroll
+    for (int m = 0; m < LA && m < NM; ++m) fr[m] = operand(m);
+    bf16x2 ones2;
+    ones2[0] = (__bf16)1.0f;
+    ones2[1] = (__bf16)1.0f;
+    bf16x8 pn[2];
+    f32x16 s;
+    l_g = 0.f;
+    // after MFMA m comes the share of the weight computation due by then
+    int chunk = 0;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (is_qk(m)) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], qf[m / 2], m == 0 ? f32x16{} : s, 0, 0, 0);
+      } else {
+        const int pv = pv_of(m), k2 = pv / NOB, ob = pv % NOB;
+        w.o[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], p[k2], w.o[ob], 0, 0, 0);
+      }
+      if (m + LA < NM) fr[m + LA] = operand(m + LA);
+#pragma unroll
+      for (; chunk < 8 && chunk * NM < 8 * (m + 1); ++chunk) {
+        const int k2 = chunk / 4, i = 2 * (chunk % 4);
+        bf16x2 pr;
+        pr[0] = (__bf16)__builtin_amdgcn_exp2f(sc[8 * k2 + i]);
+        pr[1] = (__bf16)__builtin_amdgcn_exp2f(sc[8 * k2 + i + 1]);
+        pn[k2][i] = pr[0];
+        pn[k2][i + 1] = pr[1];
+        l_g = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_g, false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s_out = s;
+    p[0] = pn[0];
+    p[1] = pn[1];
   }
   // the group's weight sum bounds each weight: raise the reference when large
   if (__builtin_expect(__any(first || l_g > kLazyThreshold), 0)) {
@@ -383,6 +464,8 @@ void attention_bf16_kernel(const AttnArgs a) {
   constexpr int NKS = D / 16;        // k-steps of the QK^T product
   constexpr int NOB = D / 32;        // 32-row blocks of O^T
   __shared__ u32x4 lds[kBuffers][T::CH];
+  // its LDS byte address, for the copies that name LDS by address
+  const unsigned lds_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)&lds[0][0];
 
   // ---- this workgroup's work ------------------------------------------------
   // The hardware deals workgroups round-robin to the 8 XCDs (workgroup w runs
@@ -467,10 +550,10 @@ void attention_bf16_kernel(const AttnArgs a) {
       lc.off = rem * kKTile;
     }
     Cursor cc = lc;                           // cursor of the tile being consumed
-    load_tile<D>(lc, tid, lds[0]);
+    load_tile<D>(lc, tid, lds_addr);
     if (n_tiles > 1) {
       advance<D>(a, B, h, lc);
-      load_tile<D>(lc, tid, lds[1]);
+      load_tile<D>(lc, tid, lds_addr + 16u * T::CH);
     }
     {
       // buffer 2 starts as zeros: the first step's deferred PV reads it
@@ -501,10 +584,12 @@ void attention_bf16_kernel(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[k2][i] = (__bf16)0.0f;
     if (active) sa = scores<D>(lds[0], lane, 0, qf);
-    int buf = 0;                              // buffer of the current tile
-    for (int t = 0; t < n_tiles; ++t) {
-      const int nbuf = buf == 2 ? 0 : buf + 1;
-      const int pbuf = buf == 0 ? 2 : buf - 1;
+    // one tile; its buffer index is a compile-time constant so that every LDS
+    // address of the steps is a per-lane base plus an immediate offset
+    auto tile = [&](auto buf_c, int t) {
+      constexpr int buf = decltype(buf_c)::value;
+      constexpr int nbuf = buf == 2 ? 0 : buf + 1;
+      constexpr int pbuf = buf == 0 ? 2 : buf - 1;
       const int valid = cc.len - cc.off;
       // group 2t: S of group 2t+1 (same tile), PV of group 2t-1 (previous tile)
       if (active)
@@ -515,16 +600,24 @@ void attention_bf16_kernel(const AttnArgs a) {
         __syncthreads();
         if (t + 2 < n_tiles) {
           advance<D>(a, B, h, lc);
-          load_tile<D>(lc, tid, lds[pbuf]);
+          load_tile<D>(lc, tid, lds_addr + 16u * T::CH * pbuf);
         }
         advance<D>(a, B, h, cc);
       }
       // group 2t+1: S of group 2t+2 (next tile), PV of group 2t (this tile)
       if (active)
         pipe_step<D>(lds[nbuf], 0, lds[buf], 0, lane, qf, c, sb, sa, p, valid - 32, false, w);
-      buf = nbuf;
+    };
+    for (int t = 0; t < n_tiles;) {
+      tile(std::integral_constant<int, 0>{}, t);
+      if (++t >= n_tiles) break;
+      tile(std::integral_constant<int, 1>{}, t);
+      if (++t >= n_tiles) break;
+      tile(std::integral_constant<int, 2>{}, t);
+      ++t;
     }
-    if (active) accumulate<D>(lds[buf == 0 ? 2 : buf - 1], lane, 1, p, w.o);
+    // the last group's PV (group 1 of the last tile)
+    if (active) accumulate<D>(lds[(n_tiles - 1) % 3], lane, 1, p, w.o);
 
     if (whole) {
       store_output<D>(a, b, h, qrow, row_ok, half, w);
