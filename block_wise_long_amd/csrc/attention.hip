@@ -246,25 +246,34 @@ __device__ __forceinline__ void accumulate(const u32x4* L, int lane, int g, cons
     }
 }
 
+// Adds a pair of weights to the running sums la, lb (two chains, so that
+// consecutive additions do not wait for each other).  The sums are taken in
+// fp32 from the unrounded exponentials, as the row sums of FlashAttention
+// are; the PV product uses the weights rounded to bf16.  (v_dot2_f32_bf16 on
+// the rounded pair costs more than the two additions on gfx950.)
+__device__ __forceinline__ void add_pair(float e0, float e1, float& la, float& lb) {
+  la += e0;
+  lb += e1;
+}
+
 // Weights of one group from its shifted scores: bf16 exp2 values packed as
-// the B operand of the PV product, and their sum (from the rounded values).
+// the B operand of the PV product, and their sum.
 __device__ __forceinline__ float weights(const f32x16& s, float shift, bf16x8 (&p)[2]) {
-  bf16x2 ones2;
-  ones2[0] = (__bf16)1.0f;
-  ones2[1] = (__bf16)1.0f;
-  float l = 0.f;
+  float la = 0.f, lb = 0.f;
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(s[8 * k2 + i] - shift);
+      const float e1 = __builtin_amdgcn_exp2f(s[8 * k2 + i + 1] - shift);
       bf16x2 pr;
-      pr[0] = (__bf16)__builtin_amdgcn_exp2f(s[8 * k2 + i] - shift);
-      pr[1] = (__bf16)__builtin_amdgcn_exp2f(s[8 * k2 + i + 1] - shift);
+      pr[0] = (__bf16)e0;
+      pr[1] = (__bf16)e1;
       p[k2][i] = pr[0];
       p[k2][i + 1] = pr[1];
-      l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l, false);
+      add_pair(e0, e1, la, lb);
     }
-  return l;
+  return la + lb;
 }
 
 // One pipeline step for group k: the matrix cores take S^T of group k+1 and
@@ -320,12 +329,9 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
     bf16x8 fr[NM];
 #pragma unroll
     for (int m = 0; m < LA && m < NM; ++m) fr[m] = operand(m);
-    bf16x2 ones2;
-    ones2[0] = (__bf16)1.0f;
-    ones2[1] = (__bf16)1.0f;
     bf16x8 pn[2];
     f32x16 s;
-    l_g = 0.f;
+    float la = 0.f, lb = 0.f;
     // after MFMA m comes the share of the weight computation due by then
     int chunk = 0;
 #pragma unroll
@@ -340,15 +346,18 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
 #pragma unroll
       for (; chunk < 8 && chunk * NM < 8 * (m + 1); ++chunk) {
         const int k2 = chunk / 4, i = 2 * (chunk % 4);
+        const float e0 = __builtin_amdgcn_exp2f(sc[8 * k2 + i]);
+        const float e1 = __builtin_amdgcn_exp2f(sc[8 * k2 + i + 1]);
         bf16x2 pr;
-        pr[0] = (__bf16)__builtin_amdgcn_exp2f(sc[8 * k2 + i]);
-        pr[1] = (__bf16)__builtin_amdgcn_exp2f(sc[8 * k2 + i + 1]);
+        pr[0] = (__bf16)e0;
+        pr[1] = (__bf16)e1;
         pn[k2][i] = pr[0];
         pn[k2][i + 1] = pr[1];
-        l_g = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_g, false);
+        add_pair(e0, e1, la, lb);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    l_g = la + lb;
     s_out = s;
     p[0] = pn[0];
     p[1] = pn[1];
