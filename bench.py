@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
 PEAK_HBM_GBS = 8000.0
+CLOCK_GHZ, N_CU = 2.4, 256
+EXP_PER_CLK_PER_CU = 16        # v_exp_f32: a wave64 every 16 clocks on each of 4 SIMDs
 ATTN_SRC = os.path.join(ROOT, "block_wise_long_amd", "csrc", "attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_d64_dit480p_traffic.md")
 
@@ -98,6 +100,33 @@ def copy_calibration(nbytes=1 << 30, reps=3):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def update_size_sweep(B, torch, sizes_mb=(16, 64, 256, 1024, 2048), reps=5):
+    """ba_block_update alone at growing sizes (bytes moved = 3 x 2 B per
+    element), with a 512 MB write between calls so that no call finds its
+    operands in the 256 MB Infinity Cache: shows where the kernel reaches the
+    HBM plateau (the per-block updates of the workloads are a few MB)."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = []
+    for mb in sizes_mb:
+        n = (mb << 20) // 6 // 8 * 8
+        x = torch.randn(n, device="cuda").to(torch.bfloat16).view(1, n)
+        eps = torch.randn(n, device="cuda").to(torch.bfloat16).view(1, n)
+        times = []
+        for _ in range(reps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            B.ba_block_update(x, eps, [143])
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        out.append({"MB": round(6.0 * n / 1e6, 1), "ms": round(ms, 4), "GBs": round(6.0 * n / (ms * 1e-3) / 1e9, 1)})
+        del x, eps
+    del flush
+    return out
 
 
 def main():
@@ -192,12 +221,15 @@ def main():
     ms_attn = float(np.mean(ms_attn_all))
     ms_update = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
 
+    update_sweep = update_size_sweep(B, torch)
+
     flops = float(cfg.flops())
     tflops_step = flops / (ms_step * 1e-3) / 1e12
     tflops_attn = flops / (ms_attn * 1e-3) / 1e12
     append_bytes = 2.0 * 2 * appended_tokens * H * D * 2    # read K,V + write K,V (valid tokens)
     update_bytes = 3.0 * cfg.update_elems * cfg.n_blocks * 2
     traffic = traffic_from_profile(cfg.name)
+    exps = float(cfg.n_blocks) * H * cfg.q_len * cfg.key_len
 
     res = {
         "metric": "block-attention TFLOP/s + % bf16 MFMA peak; latent frames/s at 1 GPU",
@@ -219,11 +251,19 @@ def main():
         "pct_bf16_peak_step": round(100 * tflops_step / PEAK_BF16_TFLOPS, 2),
         "latent_frames_per_s": round(cfg.latent_frames / (ms_step * 1e-3), 1),
         "kernel_ms": {"append": round(ms_append, 5), "attention": round(ms_attn, 5),
+                      "attention_median": round(float(np.median(ms_attn_all)), 5),
                       "attention_p10": round(float(np.percentile(ms_attn_all, 10)), 5),
                       "attention_p90": round(float(np.percentile(ms_attn_all, 90)), 5),
                       "update": round(ms_update, 5)},
+        "latent_frames_per_s_24_heads": round(cfg.latent_frames / (ms_step * 1e-3) * H / 24, 1),
         "append_GBs": round(append_bytes / (ms_append * 1e-3) / 1e9, 1),
         "update_GBs": round(update_bytes / (ms_update * 1e-3) / 1e9, 1),
+        "update_sweep": update_sweep,
+        # the softmax's second bound: one exponential per (query, valid key,
+        # head); v_exp_f32 issues at a quarter rate, 16 per clock per CU
+        "exp_rate": {"exps_per_launch": exps,
+                     "per_clk_per_cu": round(exps / (ms_attn * 1e-3) / (CLOCK_GHZ * 1e9) / N_CU, 3),
+                     "peak_per_clk_per_cu": EXP_PER_CLK_PER_CU},
         "roofline": {"bound": "mfma", "achieved": round(tflops_attn, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops_attn / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": f"attention_bf16_kernel<{D}>",

@@ -391,6 +391,9 @@ ba_status ba_block_update(void* x, const void* eps, int64_t elems_per_block, con
                           int32_t n_blocks, const ba_schedule* sched, hipStream_t stream) {
   if (n_blocks < 0) return fail(BA_ERR_INVALID_ARG, "n_blocks < 0");
   if (elems_per_block < 0) return fail(BA_ERR_INVALID_ARG, "elems_per_block < 0");
+  // one thread per 8 elements, at most 2^31 - 1 workgroups of 256 threads
+  if (elems_per_block > ((int64_t)1 << 40))
+    return fail(BA_ERR_OUT_OF_RANGE, "elems_per_block %lld > 2^40", (long long)elems_per_block);
   if (n_blocks > 0 && t_per_block == nullptr) return fail(BA_ERR_INVALID_ARG, "t_per_block is NULL");
   if (x == nullptr || eps == nullptr) return fail(BA_ERR_INVALID_ARG, "x or eps is NULL");
   if (!aligned(x, 16) || !aligned(eps, 16)) return fail(BA_ERR_INVALID_ARG, "x or eps not 16-byte aligned");

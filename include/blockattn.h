@@ -192,7 +192,8 @@ typedef struct {
  * c2 = sqrt(1 - abar_t') - sqrt(abar_t') sqrt(1 - abar_t) / sqrt(abar_t).
  * Each queued block sits at its own timestep (DualParal Abstract: blocks at
  * progressively decreasing noise levels; pith.science verdict, key_machinery).
- * x, eps: [n_blocks][elems_per_block] bf16; t_per_block: (host) n_blocks
+ * x, eps: [n_blocks][elems_per_block] bf16 (elems_per_block <= 2^40);
+ * t_per_block: (host) n_blocks
  * integers in [0, T].  Coefficients are computed on the host in fp64 and
  * applied as fp32 FMAs; the result is rounded to bf16 (nearest even).
  */

@@ -171,6 +171,8 @@ def test_update_rejects():
     assert f(FAKE + 2, FAKE, 100, t, 2, None, None) == B.BA_ERR_INVALID_ARG
     assert f(FAKE, FAKE, -1, t, 2, None, None) == B.BA_ERR_INVALID_ARG
     assert f(FAKE, FAKE, 100, None, 2, None, None) == B.BA_ERR_INVALID_ARG
+    # one thread per 8 elements must stay within the launch limits
+    assert f(FAKE, FAKE, (1 << 40) + 8, t, 2, None, None) == B.BA_ERR_OUT_OF_RANGE
 
 
 def test_status_strings():

@@ -56,6 +56,16 @@ def test_update_matches_oracle(E):
     _check(_run(x, e, ts), x, e, ts)
 
 
+def test_large_block_spans_many_workgroups():
+    # 40M elements in one block: 20k workgroups of one 16-byte vector per
+    # thread, plus the scalar head and tail
+    rng = np.random.Generator(np.random.PCG64(41))
+    E = 40_000_003
+    x = draw(rng, (1, E), 1.0, "bf16")
+    e = draw(rng, (1, E), 1.0, "bf16")
+    _check(_run(x, e, [571]), x, e, [571])
+
+
 def test_identity_is_bit_exact():
     rng = np.random.Generator(np.random.PCG64(3))
     x = draw(rng, (3, 4099), 1.0, "bf16")
