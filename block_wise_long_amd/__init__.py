@@ -48,9 +48,13 @@ class ba_block_meta(ctypes.Structure):
                 ("text_len", ctypes.c_int32)]
 
 
+BA_SCHED_DDIM, BA_SCHED_FLOW = 0, 1
+
+
 class ba_schedule(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("stride", ctypes.c_int32),
-                ("beta_start", ctypes.c_double), ("beta_end", ctypes.c_double)]
+                ("beta_start", ctypes.c_double), ("beta_end", ctypes.c_double),
+                ("kind", ctypes.c_int32), ("shift", ctypes.c_double)]
 
 
 _P = ctypes.c_void_p
@@ -271,12 +275,18 @@ def _schedule(s):
         return None
     if isinstance(s, ba_schedule):
         return ctypes.byref(s)
+    kind = s.get("kind", BA_SCHED_DDIM)
+    if kind in ("ddim", "flow"):
+        kind = BA_SCHED_FLOW if kind == "flow" else BA_SCHED_DDIM
     return ctypes.byref(ba_schedule(s.get("T", 1000), s.get("stride", 20),
-                                    s.get("beta_start", 1e-4), s.get("beta_end", 0.02)))
+                                    s.get("beta_start", 1e-4), s.get("beta_end", 0.02),
+                                    kind, s.get("shift", 1.0)))
 
 
 def ba_block_update(x, eps, t_per_block, schedule=None):
-    """In place on x ([n_blocks][elems] bf16) with eps of the same shape."""
+    """In place on x ([n_blocks][elems] bf16) with eps of the same shape (the
+    predicted velocity for a flow-matching schedule).  schedule: None, a
+    ba_schedule, or a dict of its fields (kind "ddim" or "flow")."""
     nb = len(t_per_block)
     if x.shape != eps.shape or x.shape[0] != nb:
         raise ValueError("x, eps must be [n_blocks][elems] with one timestep per block")

@@ -73,15 +73,28 @@ void schedule_or_default(const ba_schedule* s, ba_schedule* out) {
     out->stride = 20;
     out->beta_start = 1e-4;
     out->beta_end = 0.02;
+    out->kind = BA_SCHED_DDIM;
+    out->shift = 1.0;
   }
 }
 
 ba_status check_schedule(const ba_schedule& s) {
   if (s.T < 2 || s.T > 100000) return fail(BA_ERR_OUT_OF_RANGE, "schedule T=%d outside [2, 100000]", s.T);
   if (s.stride < 0) return fail(BA_ERR_OUT_OF_RANGE, "schedule stride < 0");
+  if (s.kind == BA_SCHED_FLOW) {
+    if (!(s.shift > 0.0) || !(s.shift <= 1e6)) return fail(BA_ERR_OUT_OF_RANGE, "need 0 < shift <= 1e6");
+    return BA_OK;
+  }
+  if (s.kind != BA_SCHED_DDIM) return fail(BA_ERR_INVALID_ARG, "schedule kind %d unknown", s.kind);
   if (!(s.beta_start > 0.0) || !(s.beta_end >= s.beta_start) || !(s.beta_end < 1.0))
     return fail(BA_ERR_OUT_OF_RANGE, "need 0 < beta_start <= beta_end < 1");
   return BA_OK;
+}
+
+// Flow matching: noise level of timestep t, sigma = shift u / (1 + (shift - 1) u), u = t / T.
+double flow_sigma(const ba_schedule& s, int t) {
+  const double u = (double)t / (double)s.T;
+  return s.shift * u / (1.0 + (s.shift - 1.0) * u);
 }
 
 // abar_0..abar_T of the DDPM linear beta schedule, in fp64.
@@ -132,7 +145,7 @@ const char* ba_status_string(ba_status s) {
 
 const char* ba_last_error(void) { return g_err; }
 
-int32_t ba_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int32_t ba_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 size_t ba_ring_bytes(int32_t n_slots, int32_t slot_tokens, int32_t heads, int32_t head_dim,
                      int32_t dtype) {
@@ -382,6 +395,15 @@ ba_status ba_schedule_coefficients(const ba_schedule* sched, const int32_t* t, i
     return fail(BA_ERR_INVALID_ARG, "t, c1 or c2 is NULL");
   for (int i = 0; i < n; ++i)
     if (t[i] < 0 || t[i] > s.T) return fail(BA_ERR_OUT_OF_RANGE, "t[%d] = %d outside [0, %d]", i, t[i], s.T);
+  if (s.kind == BA_SCHED_FLOW) {
+    // one Euler step of the velocity: x' = x + (sigma(t') - sigma(t)) v
+    for (int i = 0; i < n; ++i) {
+      const int tp = t[i] - s.stride > 0 ? t[i] - s.stride : 0;
+      c1[i] = 1.0f;
+      c2[i] = (float)(flow_sigma(s, tp) - flow_sigma(s, t[i]));
+    }
+    return ok();
+  }
   const std::vector<double> ab = alpha_bar(s);
   for (int i = 0; i < n; ++i) coefficients(ab, s.stride, t[i], &c1[i], &c2[i]);
   return ok();

@@ -175,12 +175,26 @@ size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_b
 
 /*
  * Noise schedule of the per-block update.  NULL selects the default
- * {T = 1000, stride = 20, beta_start = 1e-4, beta_end = 0.02}.
+ * {T = 1000, stride = 20, beta_start = 1e-4, beta_end = 0.02, BA_SCHED_DDIM}.
+ *
+ * BA_SCHED_DDIM: eps-prediction DDIM (eta = 0) on the DDPM linear beta
+ *   schedule, see ba_block_update.
+ * BA_SCHED_FLOW: velocity-prediction flow matching (rectified flow, the
+ *   family of the Wan2.1 generator the DualParal page evaluates on, named on
+ *   the pages only through flow-matching titles): noise level
+ *   sigma(t) = shift * u / (1 + (shift - 1) * u), u = t / T (shift = 1: linear),
+ *   and one Euler step x' = x + (sigma(t') - sigma(t)) * v, i.e. c1 = 1,
+ *   c2 = sigma(t') - sigma(t); the second input of ba_block_update is the
+ *   predicted velocity v.  beta_start / beta_end are not used.
  */
+typedef enum { BA_SCHED_DDIM = 0, BA_SCHED_FLOW = 1 } ba_schedule_kind;
+
 typedef struct {
   int32_t T;                  /* number of training timesteps (>= 2)         */
   int32_t stride;             /* t' = max(t - stride, 0), stride >= 0        */
-  double  beta_start, beta_end; /* 0 < beta_start <= beta_end < 1            */
+  double  beta_start, beta_end; /* DDIM: 0 < beta_start <= beta_end < 1      */
+  int32_t kind;               /* ba_schedule_kind                            */
+  double  shift;              /* FLOW: sigma shift, 0 < shift <= 1e6         */
 } ba_schedule;
 
 /*
@@ -201,7 +215,8 @@ ba_status ba_block_update(void* x, const void* eps, int64_t elems_per_block,
                           const int32_t* t_per_block, int32_t n_blocks,
                           const ba_schedule* sched, hipStream_t stream);
 
-/* Host only: the fp32 (c1, c2) pairs ba_block_update would apply. */
+/* Host only: the fp32 (c1, c2) pairs ba_block_update would apply (either
+ * schedule kind). */
 ba_status ba_schedule_coefficients(const ba_schedule* sched, const int32_t* t,
                                    int32_t n, float* c1, float* c2);
 

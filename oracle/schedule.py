@@ -15,6 +15,19 @@ beta schedule, restated from those published methods:
   x'        = sqrt(abar_t') * x0_hat + sqrt(1 - abar_t') * eps
 
 The result is rounded to bf16 once, from fp64, at the very end.
+
+Variant: velocity-prediction flow matching.  The generator the DualParal page
+evaluates on (Wan2.1) is a flow-matching model, and the pages name that family
+only through titles ("... Guidance for Flow Matching Models", "... Velocity
+for Accelerating Flow Matching Inference").  The plain reading is rectified
+flow: x_sigma = (1 - sigma) x0 + sigma eps, velocity v = eps - x0, and one
+Euler step of the probability-flow ODE,
+
+  u         = t / T,  sigma(t) = shift * u / (1 + (shift - 1) * u)
+  x'        = x + (sigma(t') - sigma(t)) * v
+
+(shift = 1 gives the linear schedule; a shift > 1 spends more steps at high
+noise, the time shift of published flow-matching samplers).
 """
 import numpy as np
 
@@ -60,14 +73,39 @@ def ddim_coefficients(t, t_prev, ab):
     return c1, c2
 
 
+def flow_sigma(t, T, shift=1.0):
+    """Noise level of timestep t under the (shifted) linear flow schedule."""
+    u = float(t) / float(T)
+    return shift * u / (1.0 + (shift - 1.0) * u)
+
+
+def flow_step(x, v, t, t_prev, T, shift=1.0):
+    """One Euler step of the flow from t to t_prev (fp64 in, fp64 out)."""
+    x = np.asarray(x, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    return x + (flow_sigma(t_prev, T, shift) - flow_sigma(t, T, shift)) * v
+
+
+def flow_coefficients(t, t_prev, T, shift=1.0):
+    """(c1, c2) with x' = c1 x + c2 v."""
+    return 1.0, flow_sigma(t_prev, T, shift) - flow_sigma(t, T, shift)
+
+
 def block_update_ref(x_bits, eps_bits, t_per_block, T=1000, beta_start=1e-4,
-                     beta_end=0.02, stride=20):
-    """x_bits, eps_bits: [n_blocks][elems] bf16 patterns -> updated bf16 patterns."""
-    ab = alpha_bar(T, beta_start, beta_end)
+                     beta_end=0.02, stride=20, kind="ddim", shift=1.0):
+    """x_bits, eps_bits: [n_blocks][elems] bf16 patterns -> updated bf16 patterns.
+    kind "ddim": eps_bits is the predicted noise; "flow": the predicted velocity."""
     x = bf16_bits_to_f64(x_bits)
     e = bf16_bits_to_f64(eps_bits)
     out = np.empty(np.shape(x_bits), dtype=np.uint16)
+    ab = alpha_bar(T, beta_start, beta_end) if kind == "ddim" else None
     for b, t in enumerate(t_per_block):
         tp = prev_timestep(t, stride)
-        out[b] = f64_to_bf16_bits(ddim_step(x[b], e[b], int(t), tp, ab))
+        if kind == "ddim":
+            y = ddim_step(x[b], e[b], int(t), tp, ab)
+        elif kind == "flow":
+            y = flow_step(x[b], e[b], int(t), tp, T, shift)
+        else:
+            raise ValueError(kind)
+        out[b] = f64_to_bf16_bits(y)
     return out

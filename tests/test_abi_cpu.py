@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert B.ba_version() == 10000
+    assert B.ba_version() == 10100
 
 
 @pytest.mark.parametrize("shape", [(2, 5400, 24, 64), (16, 5400, 24, 64), (2, 7800, 40, 128), (1, 226, 24, 64),
@@ -59,6 +59,29 @@ def test_schedule_coefficients_custom_schedule():
     for t, a, b in zip(ts, c1, c2):
         e1, e2 = S.ddim_coefficients(t, S.prev_timestep(t, 3), ab)
         assert abs(a - e1) <= 1e-6 * abs(e1) and abs(b - e2) <= 1e-6 * abs(e2) + 1e-7
+
+
+@pytest.mark.parametrize("shift", [1.0, 3.0, 5.0])
+def test_flow_coefficients_match_oracle(shift):
+    sched = {"kind": "flow", "T": 1000, "stride": 20, "shift": shift}
+    ts = [0, 1, 7, 20, 143, 500, 999, 1000]
+    c1, c2 = B.ba_schedule_coefficients(ts, sched)
+    for t, a, b in zip(ts, c1, c2):
+        e1, e2 = S.flow_coefficients(t, S.prev_timestep(t, 20), 1000, shift)
+        assert a == 1.0 and e1 == 1.0
+        assert b == np.float32(e2), (t, b, e2)     # fp64 on the host, one rounding
+
+
+def test_flow_schedule_rejects():
+    t = (ctypes.c_int32 * 1)(10)
+    c = (ctypes.c_float * 1)()
+    for shift in (0.0, -1.0, float("nan"), 2e6):
+        bad = B.ba_schedule(1000, 20, 0.0, 0.0, B.BA_SCHED_FLOW, shift)
+        assert B.raw.ba_schedule_coefficients(ctypes.byref(bad), t, 1, c, c) == B.BA_ERR_OUT_OF_RANGE
+    bad = B.ba_schedule(1000, 20, 1e-4, 0.02, 7, 1.0)
+    assert B.raw.ba_schedule_coefficients(ctypes.byref(bad), t, 1, c, c) == B.BA_ERR_INVALID_ARG
+    ok = B.ba_schedule(1000, 20, 0.0, 0.0, B.BA_SCHED_FLOW, 1.0)     # betas unused by flow
+    assert B.raw.ba_schedule_coefficients(ctypes.byref(ok), t, 1, c, c) == B.BA_OK
 
 
 def _status(fn, *args):

@@ -30,6 +30,7 @@ def _run(x_bits, e_bits, ts, sched=None):
 
 def _check(got, x, e, ts, **sched):
     T = sched.get("T", 1000)
+    flow = sched.get("kind", "ddim") == "flow"
     ab = S.alpha_bar(T, sched.get("beta_start", 1e-4), sched.get("beta_end", 0.02))
     ref = S.block_update_ref(x, e, ts, **sched)
     xf, ef = N.bf16_bits_to_f64(x), N.bf16_bits_to_f64(e)
@@ -37,8 +38,13 @@ def _check(got, x, e, ts, **sched):
     r = N.bf16_bits_to_f64(ref)
     for b, t in enumerate(ts):
         tp = S.prev_timestep(t, sched.get("stride", 20))
-        c1, c2 = S.ddim_coefficients(int(t), tp, ab)
-        exact = S.ddim_step(xf[b], ef[b], int(t), tp, ab)
+        if flow:
+            shift = sched.get("shift", 1.0)
+            c1, c2 = S.flow_coefficients(int(t), tp, T, shift)
+            exact = S.flow_step(xf[b], ef[b], int(t), tp, T, shift)
+        else:
+            c1, c2 = S.ddim_coefficients(int(t), tp, ab)
+            exact = S.ddim_step(xf[b], ef[b], int(t), tp, ab)
         e32 = 4 * 2.0 ** -24 * (np.abs(c1 * xf[b]) + np.abs(c2 * ef[b]))
         mag = np.abs(exact) + e32
         ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(mag, 2.0 ** -126))).astype(int) - 7)
@@ -94,3 +100,22 @@ def test_many_blocks_split_launches():
     x = draw(rng, (nb, 333), 1.0, "bf16")
     e = draw(rng, (nb, 333), 1.0, "bf16")
     _check(_run(x, e, ts), x, e, ts)
+
+
+@pytest.mark.parametrize("shift", [1.0, 5.0])
+def test_flow_update_matches_oracle(shift):
+    # velocity-prediction flow matching: x' = x + (sigma(t') - sigma(t)) v
+    rng = np.random.Generator(np.random.PCG64(int(shift * 7)))
+    ts = [1 + (999 * b) // 7 for b in range(8)]
+    x = draw(rng, (8, 345600), 1.0, "bf16")
+    v = draw(rng, (8, 345600), 1.0, "bf16")
+    sched = {"kind": "flow", "T": 1000, "stride": 20, "shift": shift}
+    _check(_run(x, v, ts, sched), x, v, ts, **sched)
+
+
+def test_flow_identity_is_bit_exact():
+    rng = np.random.Generator(np.random.PCG64(9))
+    x = draw(rng, (2, 1001), 1.0, "bf16")
+    v = draw(rng, (2, 1001), 1.0, "bf16")
+    got = _run(x, v, [0, 700], {"kind": "flow", "stride": 0, "shift": 3.0})
+    assert np.array_equal(got, x)

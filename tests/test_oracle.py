@@ -408,9 +408,66 @@ def pin_block_update_rounding():
     assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-30)
 
 
+def pin_flow_sigma_by_hand():
+    # linear: sigma = t / T; shift 3 at u = 1/2: 1.5 / (1 + 1) = 0.75; ends 0 and 1
+    assert S.flow_sigma(250, 1000) == 0.25 and S.flow_sigma(1000, 1000) == 1.0
+    assert S.flow_sigma(0, 1000, 3.0) == 0.0 and S.flow_sigma(1000, 1000, 3.0) == 1.0
+    assert abs(S.flow_sigma(500, 1000, 3.0) - 0.75) < 1e-15
+    # shift s maps the linear sigma u to s u / (1 + (s - 1) u): its inverse is
+    # the same map with 1 / s
+    for u in [0.1, 0.37, 0.9]:
+        s_u = S.flow_sigma(u * 1000, 1000, 5.0)
+        assert abs(S.flow_sigma(s_u * 1000, 1000, 0.2) - u) < 1e-12
+    sig = [S.flow_sigma(t, 1000, 5.0) for t in range(0, 1001, 50)]
+    assert np.all(np.diff(sig) > 0)
+
+
+def pin_flow_consistency():
+    # on the straight path x_s = (1 - s) x0 + s eps with v = eps - x0, one Euler
+    # step lands exactly on the path at the next noise level
+    rng = _rng(18)
+    x0 = rng.standard_normal(80)
+    eps = rng.standard_normal(80)
+    for shift in [1.0, 3.0, 7.5]:
+        for t in [1000, 733, 143, 20, 7]:
+            tp = S.prev_timestep(t, 20)
+            st, sp = S.flow_sigma(t, 1000, shift), S.flow_sigma(tp, 1000, shift)
+            x = (1 - st) * x0 + st * eps
+            assert np.allclose(S.flow_step(x, eps - x0, t, tp, 1000, shift), (1 - sp) * x0 + sp * eps,
+                               atol=1e-12)
+
+
+def pin_flow_trajectory_recovers_x0():
+    rng = _rng(19)
+    x0 = rng.standard_normal(40)
+    eps = rng.standard_normal(40)
+    x, t = eps.copy(), 1000          # sigma(T) = 1: pure noise
+    while t > 0:
+        tp = S.prev_timestep(t, 20)
+        x = S.flow_step(x, eps - x0, t, tp, 1000, 3.0)
+        t = tp
+    assert np.allclose(x, x0, atol=1e-12)
+
+
+def pin_flow_coefficients_and_update():
+    for t, tp in [(1000, 980), (143, 123), (5, 0)]:
+        c1, c2 = S.flow_coefficients(t, tp, 1000)
+        assert c1 == 1.0 and abs(c2 - (tp - t) / 1000) < 1e-15
+    rng = _rng(20)
+    x = N.f64_to_bf16_bits(rng.standard_normal((2, 200)))
+    v = N.f64_to_bf16_bits(rng.standard_normal((2, 200)))
+    out = S.block_update_ref(x, v, [600, 0], kind="flow", shift=3.0)
+    assert np.array_equal(out[1], x[1])          # t = 0: no step
+    sp, st = S.flow_sigma(580, 1000, 3.0), S.flow_sigma(600, 1000, 3.0)
+    exact = N.bf16_bits_to_f64(x[0]) + (sp - st) * N.bf16_bits_to_f64(v[0])
+    assert np.array_equal(out[0], N.f64_to_bf16_bits(exact))
+
+
 SCHEDULE_PINS = [pin_alpha_bar_start_and_product, pin_betas_linear, pin_two_step_schedule_by_hand,
                  pin_ddim_consistency, pin_trajectory_recovers_x0, pin_identity_and_coefficients,
-                 pin_prev_timestep, pin_bf16_rounding, pin_block_update_rounding]
+                 pin_prev_timestep, pin_bf16_rounding, pin_block_update_rounding,
+                 pin_flow_sigma_by_hand, pin_flow_consistency, pin_flow_trajectory_recovers_x0,
+                 pin_flow_coefficients_and_update]
 
 ALL_PINS = ATTENTION_PINS + RING_PINS + SCHEDULE_PINS
 
@@ -515,6 +572,20 @@ def _mut_round_truncate(orig):
     return f64_to_bf16_bits
 
 
+def _mut_flow_sign(orig):
+    def flow_step(x, v, t, t_prev, T, shift=1.0):
+        x = np.asarray(x, dtype=np.float64); v = np.asarray(v, dtype=np.float64)
+        return x - (S.flow_sigma(t_prev, T, shift) - S.flow_sigma(t, T, shift)) * v
+    return flow_step
+
+
+def _mut_flow_shift_inverted(orig):
+    def flow_sigma(t, T, shift=1.0):
+        u = float(t) / float(T)
+        return u / (shift + (1.0 - shift) * u)
+    return flow_sigma
+
+
 MUTATIONS = [
     (A, "key_set", _mut_drop_text),
     (A, "key_set", _mut_seg_off_by_one),
@@ -528,6 +599,8 @@ MUTATIONS = [
     (S, "ddim_step", _mut_c2_sign),
     (S, "prev_timestep", _mut_no_clamp),
     (N, "f64_to_bf16_bits", _mut_round_truncate),
+    (S, "flow_step", _mut_flow_sign),
+    (S, "flow_sigma", _mut_flow_shift_inverted),
 ]
 
 
