@@ -129,6 +129,48 @@ def update_size_sweep(B, torch, sizes_mb=(16, 64, 256, 1024, 2048), reps=5):
     return out
 
 
+def queue_bench(args):
+    """One JSON line for the single-GPU FIFO queue step at the shape of the
+    8-block workload: 8 queued blocks of 5400 tokens (4 latent frames) x 24
+    heads x 64, 226 text keys, T = 1000 (stride 125); every step appends the
+    blocks' K/V, runs one attention launch over all 8 blocks (each over its
+    neighbour's K/V of the previous step, its own and the text: 11026 keys),
+    updates every block at its own timestep, pops the clean head and takes a
+    new noise block at the tail."""
+    import torch
+    from block_wise_long_amd.fifo import FifoQueue
+    torch.cuda.set_device(0)
+    n, L, H, D, TXT, T = 8, 5400, 24, 64, 226, 1000
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20254)
+    lat = (torch.randn((n, L, H, D), device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
+    tk = (torch.randn((TXT, H, D), device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
+    tv = (torch.randn((TXT, H, D), device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
+    noise = (torch.randn((L, H, D), device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
+    fq = FifoQueue(lat, tk, tv, T=T)
+    for _ in range(max(args.warmup, 1)):      # from step 1 on every block has its neighbour's context
+        fq.step(noise)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        fq.step(noise)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 4.0 * n * L * (2 * L + TXT) * D * H
+    res = {"metric": "FIFO queue step: latent frames/s and attention-equivalent TFLOP/s at 1 GPU",
+           "value": round(4 / (ms * 1e-3), 1), "unit": "latent frames/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": "fifo-queue-8x480p", "n_queue": n, "block_tokens": L, "heads": H,
+                      "head_dim": D, "text": TXT, "T": T, "stride": T // n},
+           "tflops_step": round(flops / (ms * 1e-3) / 1e12, 2),
+           "pct_bf16_peak_step": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,9 +180,17 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--queue", action="store_true",
+                    help="time the single-GPU FIFO queue step (8 blocks of the 480p shape) instead")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.queue:
+        if args.gpus != 1:
+            print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+            sys.exit(2)
+        queue_bench(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))

@@ -49,6 +49,12 @@ class ba_block_meta(ctypes.Structure):
 
 
 BA_SCHED_DDIM, BA_SCHED_FLOW = 0, 1
+BA_QUEUE_MAX = 4096
+
+
+class ba_queue(ctypes.Structure):
+    _fields_ = [("n_queue", ctypes.c_int32), ("T", ctypes.c_int32), ("block_tokens", ctypes.c_int32),
+                ("text_len", ctypes.c_int32), ("step", ctypes.c_int64), ("head_id", ctypes.c_int64)]
 
 
 class ba_schedule(ctypes.Structure):
@@ -72,6 +78,11 @@ _SIGS = {
     "ba_block_update": (_I32, [_P, _P, _I64, ctypes.POINTER(_I32), _I32, ctypes.POINTER(ba_schedule), _P]),
     "ba_schedule_coefficients": (_I32, [ctypes.POINTER(ba_schedule), ctypes.POINTER(_I32), _I32,
                                         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
+    "ba_queue_init": (_I32, [ctypes.POINTER(ba_queue), _I32, _I32, _I32, _I32]),
+    "ba_queue_ring_slots": (_I32, [_I32]),
+    "ba_queue_plan": (_I32, [ctypes.POINTER(ba_queue), ctypes.POINTER(_I32), ctypes.POINTER(ba_block_meta),
+                             ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "ba_queue_advance": (_I32, [ctypes.POINTER(ba_queue)]),
     "ba_status_string": (ctypes.c_char_p, [_I32]),
     "ba_last_error": (ctypes.c_char_p, []),
     "ba_version": (_I32, []),
@@ -305,3 +316,31 @@ def ba_schedule_coefficients(t, schedule=None):
     c2 = (ctypes.c_float * max(n, 1))()
     _check(_lib.ba_schedule_coefficients(_schedule(schedule), arr, n, c1, c2), "ba_schedule_coefficients")
     return list(c1)[:n], list(c2)[:n]
+
+
+# ---- single-GPU FIFO block queue (host bookkeeping in the library) ----------
+
+def ba_queue_init(n_queue, T, block_tokens, text_len=0):
+    q = ba_queue()
+    _check(_lib.ba_queue_init(ctypes.byref(q), n_queue, T, block_tokens, text_len), "ba_queue_init")
+    return q
+
+
+def ba_queue_ring_slots(n_queue):
+    return int(_lib.ba_queue_ring_slots(n_queue))
+
+
+def ba_queue_plan(q):
+    """The next step's plan by latent slot: (write_slots, metas, t, stride)."""
+    n = q.n_queue
+    slots = (_I32 * n)()
+    metas = (ba_block_meta * n)()
+    t = (_I32 * n)()
+    stride = _I32()
+    _check(_lib.ba_queue_plan(ctypes.byref(q), slots, metas, t, ctypes.byref(stride)), "ba_queue_plan")
+    return list(slots), list(metas), list(t), int(stride.value)
+
+
+def ba_queue_advance(q):
+    _check(_lib.ba_queue_advance(ctypes.byref(q)), "ba_queue_advance")
+    return q

@@ -441,4 +441,75 @@ ba_status ba_block_update(void* x, const void* eps, int64_t elems_per_block, con
   return ok();
 }
 
+// ---- single-GPU FIFO block queue (host bookkeeping) -------------------------
+
+int32_t ba_queue_ring_slots(int32_t n_queue) {
+  return n_queue >= 1 && n_queue <= BA_QUEUE_MAX ? 2 * n_queue : 0;
+}
+
+ba_status ba_queue_init(ba_queue* q, int32_t n_queue, int32_t T, int32_t block_tokens, int32_t text_len) {
+  if (q == nullptr) return fail(BA_ERR_INVALID_ARG, "q is NULL");
+  if (n_queue < 1 || n_queue > BA_QUEUE_MAX)
+    return fail(BA_ERR_OUT_OF_RANGE, "n_queue %d outside [1, %d]", n_queue, BA_QUEUE_MAX);
+  if (T < 2 || T > 100000 || T % n_queue != 0)
+    return fail(BA_ERR_OUT_OF_RANGE, "T = %d must be in [2, 100000] and a multiple of n_queue = %d", T, n_queue);
+  if (block_tokens < 1) return fail(BA_ERR_OUT_OF_RANGE, "block_tokens < 1");
+  if (text_len < 0) return fail(BA_ERR_OUT_OF_RANGE, "text_len < 0");
+  q->n_queue = n_queue;
+  q->T = T;
+  q->block_tokens = block_tokens;
+  q->text_len = text_len;
+  q->step = 0;
+  q->head_id = 0;
+  return ok();
+}
+
+static ba_status check_queue(const ba_queue* q) {
+  if (q == nullptr) return fail(BA_ERR_INVALID_ARG, "q is NULL");
+  if (q->n_queue < 1 || q->n_queue > BA_QUEUE_MAX || q->T < 2 || q->T % q->n_queue != 0 ||
+      q->block_tokens < 1 || q->text_len < 0 || q->step < 0 || q->head_id < 0)
+    return fail(BA_ERR_INVALID_ARG, "q was not set up by ba_queue_init");
+  return BA_OK;
+}
+
+ba_status ba_queue_plan(const ba_queue* q, int32_t* write_slots, ba_block_meta* meta, int32_t* t,
+                        int32_t* stride) {
+  ba_status st = check_queue(q);
+  if (st != BA_OK) return st;
+  if (write_slots == nullptr || meta == nullptr || t == nullptr || stride == nullptr)
+    return fail(BA_ERR_INVALID_ARG, "an output array is NULL");
+  const int64_t n = q->n_queue, g = q->step;
+  const int32_t rung = q->T / q->n_queue;
+  for (int64_t m = 0; m < n; ++m) {
+    const int64_t i = ((m - q->head_id) % n + n) % n;      // queue position of latent slot m
+    const int64_t k = q->head_id + i;                      // its block id
+    write_slots[m] = (int32_t)(2 * (k % n) + (g % 2));
+    ba_block_meta& b = meta[m];
+    memset(&b, 0, sizeof(b));
+    b.q_len = q->block_tokens;
+    if (g > 0) {   // the neighbour toward the head wrote its K/V at step g - 1
+      const int64_t kn = k - 1 + n;                        // k - 1, kept non-negative
+      b.seg[b.n_segs].slot = (int32_t)(2 * (kn % n) + ((g - 1) % 2));
+      b.seg[b.n_segs].len = q->block_tokens;
+      ++b.n_segs;
+    }
+    b.seg[b.n_segs].slot = write_slots[m];
+    b.seg[b.n_segs].len = q->block_tokens;
+    ++b.n_segs;
+    b.text_slot = 0;
+    b.text_len = q->text_len;
+    t[m] = (int32_t)((i + 1) * rung);
+  }
+  *stride = rung;
+  return ok();
+}
+
+ba_status ba_queue_advance(ba_queue* q) {
+  ba_status st = check_queue(q);
+  if (st != BA_OK) return st;
+  q->head_id += 1;
+  q->step += 1;
+  return ok();
+}
+
 }  // extern "C"

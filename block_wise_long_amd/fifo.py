@@ -1,0 +1,66 @@
+"""Single-GPU FIFO block queue over the library's calls.
+
+Block-wise denoising as the pith.science verdict on "Minute-Long Videos with
+Dual Parallelisms" describes it (pith_extraction.key_machinery): the queued
+blocks sit at decreasing noise levels from tail to head, and each step
+appends a new noisy block at the tail and pops a clean one at the head.  The
+bookkeeping (which ring slot each block writes and reads, each block's
+timestep) is the library's ba_queue_*; every step of the data path runs in
+the library's kernels: ba_cache_append_batched, ba_block_attention (one
+launch over all queued blocks), ba_block_update (each block at its own t).
+
+The model between those calls is a stand-in without trained weights: a
+block's latents, viewed as [tokens][heads][head_dim], are its queries, keys
+and values, and the attention output is the prediction the update consumes
+(the noise for DDIM, the velocity for flow matching).
+"""
+import torch
+
+from . import (BA_BF16, ba_block_attention, ba_block_update, ba_cache_append, ba_cache_append_batched,
+               ba_queue_advance, ba_queue_init, ba_queue_plan, ba_queue_ring_slots, ba_ring_init)
+
+
+class FifoQueue:
+    """latents: [n_queue][tokens][heads][head_dim] bf16 on the GPU, latent
+    slot m holding the block at queue position m (the head first) at
+    timestep (m + 1) T / n_queue.  text_k, text_v: [text_len][heads][head_dim]
+    or None.  kind: "ddim" or "flow" (with shift)."""
+
+    def __init__(self, latents, text_k=None, text_v=None, T=1000, kind="ddim", shift=1.0, workspace="auto"):
+        if latents.dtype != torch.bfloat16 or latents.dim() != 4:
+            raise ValueError("latents must be [n_queue][tokens][heads][head_dim] bf16")
+        n, L, H, D = latents.shape
+        text_len = 0 if text_k is None else int(text_k.shape[0])
+        self.q = ba_queue_init(n, T, L, text_len)
+        self.ring = ba_ring_init(ba_queue_ring_slots(n), L, H, D, BA_BF16, device=latents.device)
+        self.text = None
+        if text_len:
+            self.text = ba_ring_init(1, text_len, H, D, BA_BF16, device=latents.device)
+            ba_cache_append(self.text, text_k, text_v, text_len)
+        self.x = latents
+        self.pred = torch.empty_like(latents)
+        self.T, self.kind, self.shift, self.workspace = T, kind, shift, workspace
+        self.last_plan = None
+
+    @property
+    def head_slot(self):
+        """Latent slot of the current head block."""
+        return self.q.head_id % self.q.n_queue
+
+    def step(self, new_block):
+        """One queue step.  Returns the block that left the head (clean, a new
+        tensor); new_block ([tokens][heads][head_dim] bf16, pure noise) takes
+        its latent slot as the new tail."""
+        n = self.q.n_queue
+        slots, metas, t, stride = ba_queue_plan(self.q)
+        self.last_plan = (slots, metas, t, stride)
+        # the stand-in layer: keys and values are the latents themselves
+        ba_cache_append_batched(self.ring, self.x, self.x, slots)
+        ba_block_attention(self.x, self.ring, self.text, metas, out=self.pred, workspace=self.workspace)
+        ba_block_update(self.x.view(n, -1), self.pred.view(n, -1), t,
+                        {"kind": self.kind, "T": self.T, "stride": stride, "shift": self.shift})
+        m = self.head_slot
+        done = self.x[m].clone()
+        self.x[m].copy_(new_block)
+        ba_queue_advance(self.q)
+        return done

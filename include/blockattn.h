@@ -220,6 +220,67 @@ ba_status ba_block_update(void* x, const void* eps, int64_t elems_per_block,
 ba_status ba_schedule_coefficients(const ba_schedule* sched, const int32_t* t,
                                    int32_t n, float* c1, float* c2);
 
+/*
+ * Single-GPU FIFO block queue: host bookkeeping only (no device memory, no
+ * launch).  Block-wise denoising as the pith.science verdict on the DualParal
+ * page describes it (pith_extraction.key_machinery): the queued blocks sit at
+ * monotonically decreasing noise levels from tail to head, and every step
+ * appends a new noisy block at the tail and pops a clean one at the head.
+ *
+ * Here the queue holds n_queue blocks.  Before a step, queue position i
+ * (0 = head) sits at timestep t_i = (i + 1) * T / n_queue (T divisible by
+ * n_queue); the step moves every block down one rung (stride T / n_queue), so
+ * the head reaches t = 0 and leaves, and a block of pure noise (t = T) enters
+ * at the tail.  Blocks carry absolute ids k (the head has the smallest);
+ * the caller keeps block k's latents in latent slot k mod n_queue, so the
+ * entering block takes the leaving block's slot.
+ *
+ * Feature cache (DualParal Abstract: the prior block's features are stored
+ * and reused as context): at step g block k writes its K/V into ring slot
+ *   2 * (k mod n_queue) + (g mod 2)
+ * and reads, besides its own K/V and the text, the K/V its neighbour toward
+ * the head (block k - 1) wrote at step g - 1, one step old as in the
+ * pipelined original, from slot 2 * ((k - 1) mod n_queue) + ((g - 1) mod 2):
+ * the slots a step reads and the slots it writes differ in parity, so no
+ * write of a step overwrites what the step reads (the block that leaves after
+ * step g - 1 is still read as the head's context at step g).  At step 0
+ * there is no such context.  The ring needs 2 n_queue slots of block_tokens
+ * each; the text sits in slot 0 of a text ring.
+ */
+typedef struct {
+  int32_t n_queue;            /* blocks in the queue, 1..BA_QUEUE_MAX          */
+  int32_t T;                  /* noise levels, a multiple of n_queue           */
+  int32_t block_tokens;       /* tokens (keys and queries) per block           */
+  int32_t text_len;           /* text keys, 0.. (slot 0 of the text ring)      */
+  int64_t step;               /* steps taken so far (g of the next step)       */
+  int64_t head_id;            /* absolute id of the head block                 */
+} ba_queue;
+
+#define BA_QUEUE_MAX 4096
+
+/* Fill in *q: step = 0, head_id = 0. */
+ba_status ba_queue_init(ba_queue* q, int32_t n_queue, int32_t T, int32_t block_tokens, int32_t text_len);
+
+/* Ring slots the queue's feature cache needs: 2 n_queue, or 0 if n_queue is
+ * out of range. */
+int32_t ba_queue_ring_slots(int32_t n_queue);
+
+/*
+ * The next step's plan, indexed by latent slot m = 0..n_queue-1 (host arrays
+ * of n_queue entries, owned by the caller): the ring slot the block in latent
+ * slot m writes its K/V to (write_slots[m], for ba_cache_append_batched), its
+ * key set (meta[m], for ba_block_attention: [neighbour's K/V of the previous
+ * step | own K/V | text]) and its timestep (t[m], for ba_block_update);
+ * *stride receives T / n_queue (the schedule stride of the update).
+ */
+ba_status ba_queue_plan(const ba_queue* q, int32_t* write_slots, ba_block_meta* meta, int32_t* t,
+                        int32_t* stride);
+
+/* After the step: the head (now at t = 0, latent slot head_id mod n_queue)
+ * has left and the new tail block takes its latent slot; head_id and step
+ * advance by one. */
+ba_status ba_queue_advance(ba_queue* q);
+
 const char* ba_status_string(ba_status status);
 const char* ba_last_error(void);
 int32_t     ba_version(void);   /* major*10000 + minor*100 + patch */

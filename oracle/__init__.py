@@ -26,6 +26,9 @@ Modules:
   numerics   exact bf16 <-> fp64 conversion (own implementation)
   attention  softmax(QK^T * scale) V over the [cache segments | text] key set
   ring       byte-level model of the K/V ring buffer's documented layout
-  schedule   DDPM linear betas, alpha-bar table, DDIM (eta = 0) block update
+  schedule   DDPM linear betas, alpha-bar table, DDIM (eta = 0) block update,
+             and the flow-matching (rectified flow, Euler) variant
+  queue      the single-GPU FIFO block queue: which ring slots a step writes
+             and reads, and each block's timestep
 """
-from . import numerics, attention, ring, schedule  # noqa: F401
+from . import numerics, attention, ring, schedule, queue  # noqa: F401

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import block_wise_long_amd as B
+from oracle import queue as oqueue
 from oracle import ring as oring
 from oracle import schedule as S
 
@@ -20,7 +21,7 @@ FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dere
 
 def test_exports_every_declared_symbol():
     names = B.header_symbols()
-    assert len(names) == 11
+    assert len(names) == 15
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -202,3 +203,41 @@ def test_status_strings():
     for s in range(5):
         assert B.ba_status_string(s).startswith("BA_")
     assert B.ba_status_string(99) == "BA_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("n,T,L,text", [(1, 10, 5, 0), (3, 30, 100, 16), (8, 1000, 5400, 226), (5, 1000, 64, 1)])
+def test_queue_plan_matches_oracle(n, T, L, text):
+    q = B.ba_queue_init(n, T, L, text)
+    assert B.ba_queue_ring_slots(n) == 2 * n
+    for g in range(3 * n + 4):
+        slots, metas, t, stride = B.ba_queue_plan(q)
+        ref, rstride = oqueue.plan(n, T, L, text, g, g)
+        assert stride == rstride
+        for m in range(n):
+            assert slots[m] == ref[m]["write_slot"] and t[m] == ref[m]["t"]
+            mt = metas[m]
+            segs = [(mt.seg[j].slot, mt.seg[j].len) for j in range(mt.n_segs)]
+            r = ref[m]["meta"]
+            assert (mt.q_len, segs, mt.text_slot, mt.text_len) == (r["q_len"], r["segs"], r["text_slot"],
+                                                                   r["text_len"])
+        B.ba_queue_advance(q)
+        assert q.step == g + 1 and q.head_id == g + 1
+
+
+def test_queue_rejects():
+    q = B.ba_queue()
+    f = B.raw.ba_queue_init
+    assert f(None, 3, 30, 10, 0) == B.BA_ERR_INVALID_ARG
+    assert f(ctypes.byref(q), 0, 30, 10, 0) == B.BA_ERR_OUT_OF_RANGE
+    assert f(ctypes.byref(q), 4, 30, 10, 0) == B.BA_ERR_OUT_OF_RANGE      # T not a multiple
+    assert f(ctypes.byref(q), 3, 30, 0, 0) == B.BA_ERR_OUT_OF_RANGE
+    assert f(ctypes.byref(q), 3, 30, 10, -1) == B.BA_ERR_OUT_OF_RANGE
+    assert B.ba_queue_ring_slots(0) == 0 and B.ba_queue_ring_slots(B.BA_QUEUE_MAX + 1) == 0
+    bad = B.ba_queue()                                                 # never initialised
+    s = (ctypes.c_int32 * 1)()
+    m = (B.ba_block_meta * 1)()
+    st = ctypes.c_int32()
+    assert B.raw.ba_queue_plan(ctypes.byref(bad), s, m, s, ctypes.byref(st)) == B.BA_ERR_INVALID_ARG
+    q = B.ba_queue_init(1, 10, 5)
+    assert B.raw.ba_queue_plan(ctypes.byref(q), None, m, s, ctypes.byref(st)) == B.BA_ERR_INVALID_ARG
+    assert B.raw.ba_queue_advance(None) == B.BA_ERR_INVALID_ARG

@@ -20,6 +20,7 @@ import oracle
 from oracle import attention as A
 from oracle import numerics as N
 from oracle import ring as R
+from oracle import queue as Q
 from oracle import schedule as S
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -469,7 +470,62 @@ SCHEDULE_PINS = [pin_alpha_bar_start_and_product, pin_betas_linear, pin_two_step
                  pin_flow_sigma_by_hand, pin_flow_consistency, pin_flow_trajectory_recovers_x0,
                  pin_flow_coefficients_and_update]
 
-ALL_PINS = ATTENTION_PINS + RING_PINS + SCHEDULE_PINS
+# ---------------------------------------------------------------------------
+# FIFO queue pins: simulate the queue symbolically (which block wrote which
+# ring slot at which step) and check the rules' consequences
+# ---------------------------------------------------------------------------
+
+def _simulate_queue(n_queue, T, steps):
+    written = {}                     # ring slot -> (block, step) of its last write
+    ages = {}                        # block -> list of its timesteps, step by step
+    head = 0
+    for g in range(steps):
+        pl, stride = Q.plan(n_queue, T, 10, 3, g, head)
+        assert stride * n_queue == T
+        reads, writes = [], []
+        for m, e in enumerate(pl):
+            k = e["block"]
+            assert k % n_queue == m                      # latent slot of block k
+            ages.setdefault(k, []).append(e["t"])
+            segs = e["meta"]["segs"]
+            assert segs[-1] == (e["write_slot"], 10)     # own K/V last among the segments
+            if g == 0:
+                assert len(segs) == 1
+            else:
+                assert len(segs) == 2
+                reads.append((k, segs[0][0]))
+            writes.append((k, e["write_slot"]))
+        ws = [w for _, w in writes]
+        assert len(set(ws)) == n_queue                   # no two blocks share a slot
+        assert not set(ws) & {r for _, r in reads}       # nothing read is overwritten this step
+        for k, r in reads:                               # the neighbour's K/V of the previous step
+            assert written[r] == (k - 1, g - 1), (g, k, r, written.get(r))
+        for k, w in writes:
+            written[w] = (k, g)
+        head += 1
+    return ages
+
+
+def pin_queue_context_is_neighbour_previous_step():
+    for n in [1, 2, 3, 8]:
+        _simulate_queue(n, 8 * 5 * 7 * n if n > 1 else 10, 3 * n + 5)
+
+
+def pin_queue_noise_staircase():
+    # every block that enters at the tail passes t = T, T - s, ..., s, one rung
+    # per step, and leaves right after the step at t = s
+    n, T = 4, 1000
+    ages = _simulate_queue(n, T, 30)
+    s = T // n
+    for k, ts in ages.items():
+        if k >= n and len(ts) == n:                      # entered at the tail, left at the head
+            assert ts == [T - j * s for j in range(n)], (k, ts)
+    assert ages[0] == [s] and ages[n - 1][:2] == [T, T - s]
+
+
+QUEUE_PINS = [pin_queue_context_is_neighbour_previous_step, pin_queue_noise_staircase]
+
+ALL_PINS = ATTENTION_PINS + RING_PINS + SCHEDULE_PINS + QUEUE_PINS
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -586,6 +642,33 @@ def _mut_flow_shift_inverted(orig):
     return flow_sigma
 
 
+def _mut_queue_same_step_context(orig):
+    def plan(n_queue, T, block_tokens, text_len, step, head_id):
+        out, stride = orig(n_queue, T, block_tokens, text_len, step, head_id)
+        for e in out:
+            segs = e["meta"]["segs"]
+            if len(segs) == 2:                 # read the neighbour's K/V of this step instead
+                segs[0] = (segs[0][0] ^ 1, segs[0][1])
+        return out, stride
+    return plan
+
+
+def _mut_queue_single_buffer(orig):
+    # one slot per block instead of two: the block entering at the tail takes
+    # the slot the head still reads as its context
+    def plan(n_queue, T, block_tokens, text_len, step, head_id):
+        out, stride = orig(n_queue, T, block_tokens, text_len, step, head_id)
+        for e in out:
+            k = e["block"]
+            e["write_slot"] = k % n_queue
+            segs = e["meta"]["segs"]
+            segs[-1] = (e["write_slot"], segs[-1][1])
+            if len(segs) == 2:
+                segs[0] = ((k - 1) % n_queue, segs[0][1])
+        return out, stride
+    return plan
+
+
 MUTATIONS = [
     (A, "key_set", _mut_drop_text),
     (A, "key_set", _mut_seg_off_by_one),
@@ -601,6 +684,8 @@ MUTATIONS = [
     (N, "f64_to_bf16_bits", _mut_round_truncate),
     (S, "flow_step", _mut_flow_sign),
     (S, "flow_sigma", _mut_flow_shift_inverted),
+    (Q, "plan", _mut_queue_same_step_context),
+    (Q, "plan", _mut_queue_single_buffer),
 ]
 
 
