@@ -30,5 +30,6 @@ Modules:
              and the flow-matching (rectified flow, Euler) variant
   queue      the single-GPU FIFO block queue: which ring slots a step writes
              and reads, and each block's timestep
+  projection the fused K/V producer: QKV projection and the pair rotation
 """
-from . import numerics, attention, ring, schedule, queue  # noqa: F401
+from . import numerics, attention, ring, schedule, queue, projection  # noqa: F401

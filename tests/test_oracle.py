@@ -20,6 +20,7 @@ import oracle
 from oracle import attention as A
 from oracle import numerics as N
 from oracle import ring as R
+from oracle import projection as P
 from oracle import queue as Q
 from oracle import schedule as S
 
@@ -525,7 +526,65 @@ def pin_queue_noise_staircase():
 
 QUEUE_PINS = [pin_queue_context_is_neighbour_previous_step, pin_queue_noise_staircase]
 
-ALL_PINS = ATTENTION_PINS + RING_PINS + SCHEDULE_PINS + QUEUE_PINS
+
+# ---------------------------------------------------------------------------
+# K/V producer pins
+# ---------------------------------------------------------------------------
+
+def pin_projection_brute_force():
+    # the linear layer by explicit loops on a tiny shape, split into q | k | v
+    rng = _rng(30)
+    L, dim, H, D = 3, 5, 2, 4
+    xb = N.f64_to_bf16_bits(rng.standard_normal((L, dim)))
+    wb = N.f64_to_bf16_bits(rng.standard_normal((3 * H * D, dim)))
+    x, w = N.bf16_bits_to_f64(xb), N.bf16_bits_to_f64(wb)
+    q, k, v = P.qkv_project_ref(xb, wb, H, D)
+    for t in range(L):
+        for j, out in enumerate((q, k, v)):
+            for h in range(H):
+                for d in range(D):
+                    row = j * H * D + h * D + d
+                    acc = math.fsum(x[t, c] * w[row, c] for c in range(dim))
+                    assert abs(out[t, h, d] - acc) < 1e-12
+
+
+def pin_rotation_identity_quarter_turn_and_norm():
+    rng = _rng(31)
+    y = rng.standard_normal((4, 3, 8))
+    ident = np.zeros((4, 4, 2)); ident[..., 0] = 1.0
+    assert np.array_equal(P.rotate_pairs(y, ident), y)
+    quarter = np.zeros((4, 4, 2)); quarter[..., 1] = 1.0          # multiply by i: (a, b) -> (-b, a)
+    r = P.rotate_pairs(y, quarter)
+    assert np.array_equal(r[..., 0::2], -y[..., 1::2]) and np.array_equal(r[..., 1::2], y[..., 0::2])
+    ang = rng.uniform(-7, 7, (4, 4))
+    tab = np.stack([np.cos(ang), np.sin(ang)], axis=-1)
+    r = P.rotate_pairs(y, tab)
+    n0 = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    n1 = r[..., 0::2] ** 2 + r[..., 1::2] ** 2
+    assert np.allclose(n0, n1, rtol=1e-13)
+
+
+def pin_rotation_relative_position():
+    # rotating q by angle a and k by angle b leaves <q, k> depending on a - b
+    # only: the property the rotation is used for
+    rng = _rng(32)
+    q = rng.standard_normal((1, 1, 16))
+    k = rng.standard_normal((1, 1, 16))
+    freqs = rng.uniform(0.01, 1.0, 8)
+
+    def rot(y, pos):
+        ang = (pos * freqs)[None, :]
+        return P.rotate_pairs(y, np.stack([np.cos(ang), np.sin(ang)], axis=-1))
+    d1 = float(np.sum(rot(q, 17.0) * rot(k, 5.0)))
+    d2 = float(np.sum(rot(q, 112.0) * rot(k, 100.0)))
+    d3 = float(np.sum(rot(q, 5.0) * rot(k, 17.0)))
+    assert abs(d1 - d2) < 1e-12 and abs(d1 - d3) > 1e-6
+
+
+PROJECTION_PINS = [pin_projection_brute_force, pin_rotation_identity_quarter_turn_and_norm,
+                   pin_rotation_relative_position]
+
+ALL_PINS = ATTENTION_PINS + RING_PINS + SCHEDULE_PINS + QUEUE_PINS + PROJECTION_PINS
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -669,6 +728,26 @@ def _mut_queue_single_buffer(orig):
     return plan
 
 
+def _mut_rotation_sign(orig):
+    def rotate_pairs(y, table):
+        c = np.asarray(table[..., 0])[:, None, :]; s_ = np.asarray(table[..., 1])[:, None, :]
+        a, b = y[..., 0::2], y[..., 1::2]
+        out = np.empty_like(y)
+        out[..., 0::2] = a * c + b * s_
+        out[..., 1::2] = a * s_ + b * c
+        return out
+    return rotate_pairs
+
+
+def _mut_projection_weight_not_transposed(orig):
+    def qkv_project_ref(x_bits, w_bits, heads, head_dim, table=None):
+        X = N.bf16_bits_to_f64(x_bits); W = N.bf16_bits_to_f64(w_bits)
+        Y = X @ W.reshape(W.shape[1], W.shape[0]) if W.shape[0] != W.shape[1] else X @ W
+        L, HD = X.shape[0], heads * head_dim
+        return tuple(Y[:, j * HD:(j + 1) * HD].reshape(L, heads, head_dim) for j in range(3))
+    return qkv_project_ref
+
+
 MUTATIONS = [
     (A, "key_set", _mut_drop_text),
     (A, "key_set", _mut_seg_off_by_one),
@@ -686,6 +765,8 @@ MUTATIONS = [
     (S, "flow_sigma", _mut_flow_shift_inverted),
     (Q, "plan", _mut_queue_same_step_context),
     (Q, "plan", _mut_queue_single_buffer),
+    (P, "rotate_pairs", _mut_rotation_sign),
+    (P, "qkv_project_ref", _mut_projection_weight_not_transposed),
 ]
 
 
