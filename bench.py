@@ -171,6 +171,56 @@ def queue_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def project_bench(args):
+    """One JSON line for the fused K/V producer at the 480p block's shape:
+    5400 tokens x 1536 (24 heads x 64) projected to q, k, v (4608 rows),
+    rotation on, K/V straight into a ring slot.  Compared with the plain
+    append of the same K/V."""
+    import torch
+    import block_wise_long_amd as B
+    torch.cuda.set_device(0)
+    L, H, D = 5400, 24, 64
+    dim = H * D
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20255)
+    x = torch.randn((L, dim), device="cuda", generator=gen).to(torch.bfloat16)
+    w = (torch.randn((3 * H * D, dim), device="cuda", generator=gen) * dim ** -0.5).to(torch.bfloat16)
+    pos = torch.arange(L, device="cuda", dtype=torch.float32)[:, None]
+    freq = 10000.0 ** (-torch.arange(D // 2, device="cuda", dtype=torch.float32) * 2 / D)[None, :]
+    rope = torch.stack([torch.cos(pos * freq), torch.sin(pos * freq)], dim=-1).contiguous()
+    ring = B.ba_ring_init(2, L, H, D, B.BA_BF16)
+    q = torch.empty((L, H, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((1, L, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_proj = timed(lambda: B.ba_qkv_project(x, w, ring, 1, q=q, rope=rope))
+    ms_append = timed(lambda: B.ba_cache_append_batched(ring, k, k, [0]))
+    flops = 2.0 * L * dim * 3 * H * D
+    tf = flops / (ms_proj * 1e-3) / 1e12
+    res = {"metric": "fused K/V producer TFLOP/s (QKV projection + rotation + ring layout) at 1 GPU",
+           "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_proj, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "qkv-producer-480p-block", "tokens": L, "dim": dim, "rows": 3 * H * D,
+                      "heads": H, "head_dim": D, "rotation": True},
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "kernel": f"project_kernel<{D}>", "flop_per_launch": flops},
+           "append_ms_same_kv": round(ms_append, 5)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,9 +232,17 @@ def main():
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--queue", action="store_true",
                     help="time the single-GPU FIFO queue step (8 blocks of the 480p shape) instead")
+    ap.add_argument("--project", action="store_true",
+                    help="time the fused K/V producer (QKV projection of the 480p block) instead")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.project:
+        if args.gpus != 1:
+            print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+            sys.exit(2)
+        project_bench(args)
         return
     if args.queue:
         if args.gpus != 1:

@@ -78,6 +78,7 @@ _SIGS = {
     "ba_block_update": (_I32, [_P, _P, _I64, ctypes.POINTER(_I32), _I32, ctypes.POINTER(ba_schedule), _P]),
     "ba_schedule_coefficients": (_I32, [ctypes.POINTER(ba_schedule), ctypes.POINTER(_I32), _I32,
                                         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
+    "ba_qkv_project": (_I32, [_P, _I32, _I32, _P, _P, ctypes.POINTER(ba_ring), _I32, _P, _P]),
     "ba_queue_init": (_I32, [ctypes.POINTER(ba_queue), _I32, _I32, _I32, _I32]),
     "ba_queue_ring_slots": (_I32, [_I32]),
     "ba_queue_plan": (_I32, [ctypes.POINTER(ba_queue), ctypes.POINTER(_I32), ctypes.POINTER(ba_block_meta),
@@ -344,3 +345,25 @@ def ba_queue_plan(q):
 def ba_queue_advance(q):
     _check(_lib.ba_queue_advance(ctypes.byref(q)), "ba_queue_advance")
     return q
+
+
+# ---- fused K/V producer -------------------------------------------------------
+
+def ba_qkv_project(x, w, cache, slot, q=None, rope=None):
+    """x: [n_tokens][dim] bf16, w: [3 * heads * head_dim][dim] bf16 (a linear
+    layer's weight, rows q | k | v); K and V go to ring slot `slot`, Q to q
+    ([n_tokens][heads][head_dim] bf16) when given.  rope: optional
+    [n_tokens][head_dim / 2][2] fp32 (cos, sin) table for q and k."""
+    if x.dim() != 2 or w.dim() != 2 or w.shape[1] != x.shape[1]:
+        raise ValueError("x must be [n_tokens][dim] and w [3 * heads * head_dim][dim]")
+    d = cache.desc
+    if w.shape[0] != 3 * d.heads * d.head_dim:
+        raise ValueError("w must have 3 * heads * head_dim rows")
+    if q is not None and q.numel() < x.shape[0] * d.heads * d.head_dim:
+        raise ValueError("q too small")
+    if rope is not None and (rope.dtype != torch.float32 or rope.numel() < x.shape[0] * d.head_dim):
+        raise ValueError("rope must be fp32 [n_tokens][head_dim / 2][2]")
+    _check(_lib.ba_qkv_project(_dev(x, "x"), x.shape[0], x.shape[1], _dev(w, "w"),
+                               _dev(q, "q") if q is not None else None, ctypes.byref(d), slot,
+                               _dev(rope, "rope") if rope is not None else None, _stream()),
+           "ba_qkv_project")

@@ -512,4 +512,42 @@ ba_status ba_queue_advance(ba_queue* q) {
   return ok();
 }
 
+// ---- fused K/V producer -----------------------------------------------------
+
+ba_status ba_qkv_project(const void* x, int32_t n_tokens, int32_t dim, const void* w, void* q,
+                         const ba_ring* cache, int32_t slot, const float* rope, hipStream_t stream) {
+  ba_status st = check_ring(cache, "cache");
+  if (st != BA_OK) return st;
+  if (cache->dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "the producer writes bf16 rings only");
+  if (x == nullptr || w == nullptr) return fail(BA_ERR_INVALID_ARG, "x or w is NULL");
+  if (!aligned(x, 16) || !aligned(w, 16) || (q && !aligned(q, 16)))
+    return fail(BA_ERR_INVALID_ARG, "x, w or q not 16-byte aligned");
+  if (rope && !aligned(rope, 8)) return fail(BA_ERR_INVALID_ARG, "rope not 8-byte aligned");
+  if (slot < 0 || slot >= cache->n_slots)
+    return fail(BA_ERR_OUT_OF_RANGE, "slot %d outside [0, %d)", slot, cache->n_slots);
+  if (n_tokens < 1 || n_tokens > cache->slot_tokens)
+    return fail(BA_ERR_OUT_OF_RANGE, "n_tokens %d outside [1, %d]", n_tokens, cache->slot_tokens);
+  if (dim < 64 || dim % 64 != 0 || (int64_t)n_tokens * dim >= ((int64_t)1 << 30))
+    return fail(BA_ERR_OUT_OF_RANGE, "dim %d must be a positive multiple of 64 (n_tokens * dim < 2^30)", dim);
+  const int64_t n_ch = 3 * (int64_t)cache->heads * cache->head_dim;
+  if (n_ch * dim >= ((int64_t)1 << 30)) return fail(BA_ERR_OUT_OF_RANGE, "weight too large");
+  ba::ProjArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(w);
+  a.q = static_cast<uint16_t*>(q);
+  a.ring = static_cast<uint16_t*>(cache->base);
+  a.rope = rope;
+  a.n_tokens = n_tokens;
+  a.dim = dim;
+  a.heads = cache->heads;
+  a.t_pad = cache->slot_stride_tokens;
+  a.slot = slot;
+  a.n_ch = (int32_t)n_ch;
+  a.ch_begin = q ? 0 : cache->heads * cache->head_dim;
+  hipError_t e = ba::launch_project(a, cache->head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return ok();
+}
+
 }  // extern "C"

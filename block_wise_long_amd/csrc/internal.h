@@ -123,6 +123,45 @@ size_t attention_partial_bytes(int head_dim);   // workspace bytes of one partia
 hipError_t attention_bf16_resident(int head_dim, int* per_cu);   // workgroups per CU
 int attention_f32_q_tile();
 
+// ---- fused K/V producer (QKV projection) --------------------------------------
+struct ProjArgs {
+  const uint16_t* x;        // [n_tokens][dim] bf16
+  const uint16_t* w;        // [3 * heads * head_dim][dim] bf16 (rows q | k | v)
+  uint16_t* q;              // [n_tokens][heads][head_dim] bf16, or null (q rows skipped)
+  uint16_t* ring;           // cache ring base
+  const float* rope;        // [n_tokens][head_dim / 2][2] (cos, sin), or null
+  int32_t n_tokens;
+  int32_t dim;              // multiple of 64
+  int32_t heads;
+  int32_t t_pad;            // ring slot token stride
+  int32_t slot;             // ring slot K and V go to
+  int32_t ch_begin;         // first output row computed: 0, or heads * head_dim without q
+  int32_t n_ch;             // 3 * heads * head_dim
+  int32_t pad_;
+};
+hipError_t launch_project(const ProjArgs& a, int head_dim, hipStream_t s);
+#ifndef BA_PROJ_TOK
+#define BA_PROJ_TOK 256
+#endif
+#ifndef BA_PROJ_CH
+#define BA_PROJ_CH 128
+#endif
+#ifndef BA_PROJ_K
+#define BA_PROJ_K 32
+#endif
+#ifndef BA_PROJ_WPS
+#define BA_PROJ_WPS 2
+#endif
+#ifndef BA_PROJ_WAVES_T
+#define BA_PROJ_WAVES_T 2
+#endif
+#ifndef BA_PROJ_STAGES
+#define BA_PROJ_STAGES 3
+#endif
+constexpr int kProjTokTile = BA_PROJ_TOK;        // tokens per workgroup tile of the producer
+constexpr int kProjChTile = BA_PROJ_CH;          // output rows per workgroup tile
+constexpr int kProjKStep = BA_PROJ_K;            // input dims per LDS stage
+
 // ---- block update -----------------------------------------------------------
 struct UpdateArgs {
   uint16_t* x;              // [n_blocks][elems] bf16

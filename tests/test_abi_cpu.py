@@ -21,7 +21,7 @@ FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dere
 
 def test_exports_every_declared_symbol():
     names = B.header_symbols()
-    assert len(names) == 15
+    assert len(names) == 16
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -241,3 +241,20 @@ def test_queue_rejects():
     q = B.ba_queue_init(1, 10, 5)
     assert B.raw.ba_queue_plan(ctypes.byref(q), None, m, s, ctypes.byref(st)) == B.BA_ERR_INVALID_ARG
     assert B.raw.ba_queue_advance(None) == B.BA_ERR_INVALID_ARG
+
+
+def test_project_rejects():
+    f = B.raw.ba_qkv_project
+    r = _ring(n_slots=2, slot_tokens=100, heads=2, head_dim=64)
+    rr = ctypes.byref(r)
+    assert f(None, 100, 128, FAKE, FAKE, rr, 1, None, None) == B.BA_ERR_INVALID_ARG
+    assert f(FAKE, 100, 128, None, FAKE, rr, 1, None, None) == B.BA_ERR_INVALID_ARG
+    assert f(FAKE + 2, 100, 128, FAKE, FAKE, rr, 1, None, None) == B.BA_ERR_INVALID_ARG
+    assert f(FAKE, 100, 128, FAKE, FAKE, rr, 1, FAKE + 4, None) == B.BA_ERR_INVALID_ARG     # rope alignment
+    assert f(FAKE, 100, 128, FAKE, FAKE, rr, 2, None, None) == B.BA_ERR_OUT_OF_RANGE        # slot
+    assert f(FAKE, 101, 128, FAKE, FAKE, rr, 1, None, None) == B.BA_ERR_OUT_OF_RANGE        # n_tokens
+    assert f(FAKE, 0, 128, FAKE, FAKE, rr, 1, None, None) == B.BA_ERR_OUT_OF_RANGE
+    assert f(FAKE, 100, 96, FAKE, FAKE, rr, 1, None, None) == B.BA_ERR_OUT_OF_RANGE         # dim % 64
+    assert f(FAKE, 100, 0, FAKE, FAKE, rr, 1, None, None) == B.BA_ERR_OUT_OF_RANGE
+    r32 = _ring(n_slots=2, slot_tokens=100, heads=2, head_dim=64, dtype=B.BA_F32)
+    assert f(FAKE, 100, 128, FAKE, FAKE, ctypes.byref(r32), 1, None, None) == B.BA_ERR_UNSUPPORTED

@@ -1,0 +1,118 @@
+"""The fused K/V producer (ba_qkv_project) through the C ABI against the fp64
+oracle: Q in its buffer, K and V in the ring slot in the cache's layout with
+the slot's tail zeroed, every other slot untouched.
+
+The kernel accumulates the dim products in fp32 on the matrix cores (and
+rotates in fp32); the oracle rounds the exact fp64 value once.  Bar: every
+element within one bf16 ulp of the exact value plus the fp32 error bound
+e = 2^-21 * sum_c |x_c w_c| (covering the accumulation and the rotation),
+and at least 99 % of the elements bit-exact."""
+import numpy as np
+import pytest
+
+from _util import ring_bytes, to_dev, to_host_bits
+from oracle import numerics as N
+from oracle import projection as P
+from oracle import ring as oring
+from workloads import draw
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(got_bits, exact, bound):
+    got = N.bf16_bits_to_f64(got_bits)
+    mag = np.abs(exact) + bound
+    ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(mag, 2.0 ** -126))).astype(int) - 7)
+    bad = np.abs(got - exact) > ulp + bound
+    assert not bad.any(), (got[bad][:4], exact[bad][:4])
+    frac = float(np.mean(got_bits == N.f64_to_bf16_bits(exact)))
+    assert frac >= 0.99, f"bit-exact fraction {frac:.4f}"
+
+
+def _case(L, dim, H, D, slot, n_slots, with_q, with_rope, seed):
+    import torch
+    import block_wise_long_amd as B
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = draw(rng, (L, dim), 1.0, "bf16")
+    w = draw(rng, (3 * H * D, dim), dim ** -0.5, "bf16")
+    table = None
+    if with_rope:
+        ang = rng.uniform(-40.0, 40.0, (L, D // 2))
+        table = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    ring = B.ba_ring_init(n_slots, L + 37, H, D, B.BA_BF16)
+    q = torch.full((L, H, D), float("nan"), dtype=torch.bfloat16, device="cuda") if with_q else None
+    B.ba_qkv_project(to_dev(x, "bf16"), to_dev(w, "bf16"), ring, slot, q=q,
+                     rope=torch.from_numpy(table).cuda() if with_rope else None)
+    torch.cuda.synchronize()
+    qe, ke, ve = P.qkv_project_ref(x, w, H, D, table)
+    absx = np.abs(N.bf16_bits_to_f64(x))
+    absw = np.abs(N.bf16_bits_to_f64(w))
+    bound = (2.0 ** -21) * (absx @ absw.T)                       # [L][3HD]
+    HD = H * D
+    bq, bk, bv = (bound[:, j * HD:(j + 1) * HD].reshape(L, H, D) for j in range(3))
+    if with_rope:   # a rotated pair mixes both members' errors
+        def partner(b):
+            return b.reshape(L, H, D // 2, 2)[..., ::-1].reshape(L, H, D)
+        bq = bq + partner(bq)
+        bk = bk + partner(bk)
+    if with_q:
+        _check(to_host_bits(q), qe, bq)
+    # K and V read back through the ring model's documented offsets
+    model = oring.RingModel(n_slots, L + 37, H, D, "bf16")
+    buf = np.frombuffer(ring_bytes(ring), dtype=np.uint16)
+    got_k = np.empty((L, H, D), np.uint16)
+    got_v = np.empty((L, H, D), np.uint16)
+    for h in range(H):
+        for t in range(L):
+            got_k[t, h] = buf[[model.k_offset(slot, h, t, d) for d in range(D)]]
+            got_v[t, h] = buf[[model.v_offset(slot, h, t, d) for d in range(D)]]
+    _check(got_k, ke, bk)
+    _check(got_v, ve, bv)
+    # the slot's tail is zero and no other slot was touched
+    mask = np.ones(buf.size, bool)
+    for h in range(H):
+        for t in range(L):
+            for d in range(D):
+                mask[model.k_offset(slot, h, t, d)] = False
+                mask[model.v_offset(slot, h, t, d)] = False
+    assert not buf[mask].any()
+
+
+@pytest.mark.parametrize("L,dim,H,D,with_q,with_rope", [
+    (300, 128, 2, 64, True, True),      # ragged token tile, rotation
+    (300, 128, 2, 64, True, False),
+    (257, 192, 3, 64, True, True),      # odd heads: a channel tile spans q and k
+    (200, 256, 2, 128, True, True),
+    (130, 64, 1, 64, False, False),     # no q: only the k and v rows are computed
+])
+def test_producer_matches_oracle(L, dim, H, D, with_q, with_rope):
+    _case(L, dim, H, D, slot=1, n_slots=3, with_q=with_q, with_rope=with_rope, seed=L + dim + D)
+
+
+def test_producer_feeds_attention_like_append():
+    # K/V produced into a slot equal, bit for bit, the same K/V appended there
+    import torch
+    import block_wise_long_amd as B
+    rng = np.random.Generator(np.random.PCG64(5))
+    L, dim, H, D = 190, 128, 2, 64
+    x = to_dev(draw(rng, (L, dim), 1.0, "bf16"), "bf16")
+    w = to_dev(draw(rng, (3 * H * D, dim), dim ** -0.5, "bf16"), "bf16")
+    r1 = B.ba_ring_init(2, L, H, D, B.BA_BF16)
+    r2 = B.ba_ring_init(2, L, H, D, B.BA_BF16)
+    q = torch.empty((L, H, D), dtype=torch.bfloat16, device="cuda")
+    B.ba_qkv_project(x, w, r1, 1, q=q)
+    # the same projection in three calls' worth of pieces: q from the first,
+    # k and v extracted from r1 and appended into r2's slot 1 through the
+    # append path; the two rings must be byte-identical
+    torch.cuda.synchronize()
+    model = oring.RingModel(2, L, H, D, "bf16")
+    buf = np.frombuffer(ring_bytes(r1), dtype=np.uint16)
+    k = np.empty((L, H, D), np.uint16)
+    v = np.empty((L, H, D), np.uint16)
+    for h in range(H):
+        for t in range(L):
+            k[t, h] = buf[[model.k_offset(1, h, t, d) for d in range(D)]]
+            v[t, h] = buf[[model.v_offset(1, h, t, d) for d in range(D)]]
+    B.ba_cache_append_batched(r2, to_dev(k[None], "bf16"), to_dev(v[None], "bf16"), [1])
+    torch.cuda.synchronize()
+    assert ring_bytes(r1) == ring_bytes(r2)
