@@ -187,7 +187,8 @@ def project_bench(args):
     w = (torch.randn((3 * H * D, dim), device="cuda", generator=gen) * dim ** -0.5).to(torch.bfloat16)
     pos = torch.arange(L, device="cuda", dtype=torch.float32)[:, None]
     freq = 10000.0 ** (-torch.arange(D // 2, device="cuda", dtype=torch.float32) * 2 / D)[None, :]
-    rope = torch.stack([torch.cos(pos * freq), torch.sin(pos * freq)], dim=-1).contiguous()
+    ang = (pos * freq).t()                                    # pair-major: [D/2][L]
+    rope = torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).contiguous()
     ring = B.ba_ring_init(2, L, H, D, B.BA_BF16)
     q = torch.empty((L, H, D), dtype=torch.bfloat16, device="cuda")
     k = torch.empty((1, L, H, D), dtype=torch.bfloat16, device="cuda")
@@ -206,6 +207,10 @@ def project_bench(args):
 
     ms_proj = timed(lambda: B.ba_qkv_project(x, w, ring, 1, q=q, rope=rope))
     ms_append = timed(lambda: B.ba_cache_append_batched(ring, k, k, [0]))
+    # context only: the vendor library's linear layer on the same operands
+    # (plain [tokens][rows] output, no rotation, no ring layout)
+    y = torch.empty((L, 3 * H * D), dtype=torch.bfloat16, device="cuda")
+    ms_lib = timed(lambda: torch.mm(x, w.t(), out=y))
     flops = 2.0 * L * dim * 3 * H * D
     tf = flops / (ms_proj * 1e-3) / 1e12
     res = {"metric": "fused K/V producer TFLOP/s (QKV projection + rotation + ring layout) at 1 GPU",
@@ -217,7 +222,9 @@ def project_bench(args):
            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                         "kernel": f"project_kernel<{D}>", "flop_per_launch": flops},
-           "append_ms_same_kv": round(ms_append, 5)}
+           "append_ms_same_kv": round(ms_append, 5),
+           "library_mm_ms": round(ms_lib, 5),
+           "library_mm_tflops": round(flops / (ms_lib * 1e-3) / 1e12, 2)}
     print(json.dumps(res), flush=True)
 
 

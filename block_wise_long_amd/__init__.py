@@ -353,7 +353,7 @@ def ba_qkv_project(x, w, cache, slot, q=None, rope=None):
     """x: [n_tokens][dim] bf16, w: [3 * heads * head_dim][dim] bf16 (a linear
     layer's weight, rows q | k | v); K and V go to ring slot `slot`, Q to q
     ([n_tokens][heads][head_dim] bf16) when given.  rope: optional
-    [n_tokens][head_dim / 2][2] fp32 (cos, sin) table for q and k."""
+    [head_dim / 2][n_tokens][2] fp32 (cos, sin) table for q and k, pair-major."""
     if x.dim() != 2 or w.dim() != 2 or w.shape[1] != x.shape[1]:
         raise ValueError("x must be [n_tokens][dim] and w [3 * heads * head_dim][dim]")
     d = cache.desc
@@ -362,7 +362,7 @@ def ba_qkv_project(x, w, cache, slot, q=None, rope=None):
     if q is not None and q.numel() < x.shape[0] * d.heads * d.head_dim:
         raise ValueError("q too small")
     if rope is not None and (rope.dtype != torch.float32 or rope.numel() < x.shape[0] * d.head_dim):
-        raise ValueError("rope must be fp32 [n_tokens][head_dim / 2][2]")
+        raise ValueError("rope must be fp32 [head_dim / 2][n_tokens][2]")
     _check(_lib.ba_qkv_project(_dev(x, "x"), x.shape[0], x.shape[1], _dev(w, "w"),
                                _dev(q, "q") if q is not None else None, ctypes.byref(d), slot,
                                _dev(rope, "rope") if rope is not None else None, _stream()),

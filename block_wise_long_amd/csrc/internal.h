@@ -144,7 +144,7 @@ hipError_t launch_project(const ProjArgs& a, int head_dim, hipStream_t s);
 #define BA_PROJ_TOK 256
 #endif
 #ifndef BA_PROJ_CH
-#define BA_PROJ_CH 128
+#define BA_PROJ_CH 256
 #endif
 #ifndef BA_PROJ_K
 #define BA_PROJ_K 32
@@ -153,10 +153,13 @@ hipError_t launch_project(const ProjArgs& a, int head_dim, hipStream_t s);
 #define BA_PROJ_WPS 2
 #endif
 #ifndef BA_PROJ_WAVES_T
-#define BA_PROJ_WAVES_T 2
+#define BA_PROJ_WAVES_T 4
 #endif
 #ifndef BA_PROJ_STAGES
 #define BA_PROJ_STAGES 3
+#endif
+#ifndef BA_PROJ_GROUP
+#define BA_PROJ_GROUP 8
 #endif
 constexpr int kProjTokTile = BA_PROJ_TOK;        // tokens per workgroup tile of the producer
 constexpr int kProjChTile = BA_PROJ_CH;          // output rows per workgroup tile

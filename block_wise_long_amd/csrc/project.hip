@@ -11,6 +11,8 @@
 // output channels: the rotation of adjacent pairs stays inside a lane, K rows
 // go out as 8-byte stores and V^T columns as one 2-byte store per lane, lanes
 // walking consecutive tokens.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ba {
@@ -36,6 +38,14 @@ constexpr int kLoads = kStageChunks / kThreads;        // per thread and stage
 constexpr int kWLoads = kWRows * kRowChunks / kThreads;
 constexpr int kStages = BA_PROJ_STAGES;
 static_assert(kStageChunks % kThreads == 0 && (kWRows * kRowChunks) % kThreads == 0, "tile shape");
+// epilogue staging (bf16 elements; pitches padded off the 128-byte bank period)
+constexpr int kEpiTokPitch = 64 + 8;                   // [token][64 dims]
+constexpr int kEpiDimPitch = kWaveToks + 8;            // [64 dims][tokens]
+constexpr int kEpiWaveElems = (kWaveToks * kEpiTokPitch > 64 * kEpiDimPitch ? kWaveToks * kEpiTokPitch
+                                                                             : 64 * kEpiDimPitch);
+static_assert((kThreads / 64) * kEpiWaveElems * 2 <= kStages * kStageChunks * 16, "epilogue fits the LDS stages");
+static_assert(kWaveRows % 64 == 0 && kWaveToks % 32 == 0 && kWaveToks <= 512, "wave tile");
+static_assert(kEpiWaveElems % 8 == 0, "16-byte aligned wave regions");
 static_assert(kRowChunks == 4 || kRowChunks == 8, "row length");
 
 // XOR swizzle of the 16-byte chunks of a row: the lanes of an MFMA operand
@@ -116,7 +126,25 @@ __device__ __forceinline__ void wait_newer(int n) {   // n in [0, kStages - 2]
     default: wait_vm<0>(); break;
   }
 }
-static_assert(kStages >= 2 && kStages <= 7, "stages");
+static_assert(kStages >= 3 && kStages <= 7, "stages: the next stage is issued a full stage before it is published");
+
+// Workgroup -> output tile.  Workgroup w runs on XCD w % 8, whose L2 is its
+// own; XCD x takes a contiguous run of tiles in an order that walks bands of
+// kGroup token tiles channel tile by channel tile, so the workgroups resident
+// on one XCD at a time share most of their input rows and weight rows in
+// that XCD's L2.
+constexpr int kGroup = BA_PROJ_GROUP;
+struct TileXY { int tt, ct; };
+__device__ __forceinline__ TileXY tile_of(int w, int n_tt, int n_ct) {
+  const int n = n_tt * n_ct;
+  const int x = w & 7, j = w >> 3;
+  const int q = n >> 3, r = n & 7;
+  const int rank = x * q + (x < r ? x : r) + j;     // this XCD's share starts at x*q + min(x, r)
+  const int band = rank / (kGroup * n_ct);
+  const int g = min(kGroup, n_tt - band * kGroup);  // token tiles in this band
+  const int local = rank - band * kGroup * n_ct;
+  return {band * kGroup + local % g, local / g};
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BA_PROJ_WPS, BA_PROJ_WPS)))
@@ -129,8 +157,10 @@ void project_kernel(const ProjArgs a) {
   const int wave = tid >> 6;
   const int cw = wave & 1;             // weight rows kWaveRows cw .. of the tile
   const int tw = wave >> 1;            // token rows kWaveToks tw .. of the tile (0 .. kWavesT - 1)
-  const int t0 = blockIdx.x * kProjTokTile;
-  const int ch0 = a.ch_begin + blockIdx.y * kProjChTile;
+  const TileXY tile = tile_of(blockIdx.x, (a.t_pad + kProjTokTile - 1) / kProjTokTile,
+                              (a.n_ch - a.ch_begin + kProjChTile - 1) / kProjChTile);
+  const int t0 = tile.tt * kProjTokTile;
+  const int ch0 = a.ch_begin + tile.ct * kProjChTile;
   const int n_k = a.dim / kKStep;
 
   f32x16 acc[kRB][kTB];
@@ -141,8 +171,11 @@ void project_kernel(const ProjArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cb][tb][i] = 0.f;
 
-  // kStages buffers: kStages - 1 stages in flight ahead of the one consumed;
-  // stage s holds input dims [kKStep s, kKStep (s + 1))
+  // kStages LDS buffers; stage s holds input dims [kKStep s, kKStep (s + 1)).
+  // Software pipeline inside a wave: the operands of the next 16-dim step are
+  // read from LDS while the matrix cores work on the current one (two register
+  // sets), and the barrier that publishes the next stage sits between the two,
+  // so a wave's MFMA stream never waits on its own LDS reads.
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
     if (s < n_k) load_stage(a, ch0, t0, s * kKStep, tid, lds_addr + 16u * kStageChunks * s);
@@ -151,107 +184,165 @@ void project_kernel(const ProjArgs a) {
     wait_newer(issued - 1);                             // stage 0 has landed
   }
   __syncthreads();
-  for (int kt = 0; kt < n_k; ++kt) {
-    const int st = kt % kStages;
-    const int ahead = kt + kStages - 1;
-    if (ahead < n_k)     // its buffer was last read at kt - 1 (barrier below)
-      load_stage(a, ch0, t0, ahead * kKStep, tid, lds_addr + 16u * kStageChunks * (ahead % kStages));
-    const u32x4* L = lds[st];
+
+  bf16x8 fw[2][kRB], fx[2][kTB];
+  auto read_frag = [&](int f, const u32x4* L, int ks) {
 #pragma unroll
-    for (int ks = 0; ks < kKStep / 16; ++ks) {
-      bf16x8 wa[kRB], xb[kTB];
+    for (int cb = 0; cb < kRB; ++cb)
+      fw[f][cb] = as_bf16x8(L[lds_idx(kWaveRows * cw + 32 * cb + (lane & 31), 2 * ks + half)]);
 #pragma unroll
-      for (int cb = 0; cb < kRB; ++cb)
-        wa[cb] = as_bf16x8(L[lds_idx(kWaveRows * cw + 32 * cb + (lane & 31), 2 * ks + half)]);
+    for (int tb = 0; tb < kTB; ++tb)
+      fx[f][tb] = as_bf16x8(L[kWRows * kRowChunks + lds_idx(kWaveToks * tw + 32 * tb + (lane & 31), 2 * ks + half)]);
+  };
+  constexpr int kSub = kKStep / 16;                    // 16-dim steps per stage (even)
+  static_assert(kSub % 2 == 0, "register sets alternate by step parity");
+  // one stage; the last one has no next stage to publish or read, and is a
+  // copy of its own so that no branch joins the two register sets' waits
+  auto stage = [&](int kt, auto is_last) {
+    const u32x4* L = lds[kt % kStages];
 #pragma unroll
-      for (int tb = 0; tb < kTB; ++tb)
-        xb[tb] = as_bf16x8(L[kWRows * kRowChunks + lds_idx(kWaveToks * tw + 32 * tb + (lane & 31), 2 * ks + half)]);
+    for (int ks = 0; ks < kSub; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < kSub) {
+        read_frag(nxt, L, ks + 1);
+      } else if constexpr (!decltype(is_last)::value) {
+        // publish stage kt + 1 (the stages issued after it may stay in
+        // flight); past the barrier every wave has finished iteration kt - 1,
+        // whose reads of buffer (kt - 1) mod kStages all completed before its
+        // MFMAs, so that buffer takes stage kt + kStages - 1
+        const int ahead = kt + kStages - 2;               // newest stage issued so far
+        wait_newer((ahead < n_k ? ahead : n_k - 1) - (kt + 1));
+        __syncthreads();
+        if (kt + kStages - 1 < n_k)
+          load_stage(a, ch0, t0, (kt + kStages - 1) * kKStep, tid,
+                     lds_addr + 16u * kStageChunks * ((kt + kStages - 1) % kStages));
+        read_frag(nxt, lds[(kt + 1) % kStages], 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cb = 0; cb < kRB; ++cb)
 #pragma unroll
         for (int tb = 0; tb < kTB; ++tb)
-          acc[cb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[cb], xb[tb], acc[cb][tb], 0, 0, 0);
+          acc[cb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][cb], fx[cur][tb], acc[cb][tb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < n_k) {
-      // publish stage kt + 1: the stages issued after it may stay in flight
-      const int last = ahead < n_k ? ahead : n_k - 1;
-      wait_newer(last - (kt + 1));
-      __syncthreads();
-    }
-  }
+  };
+  read_frag(0, lds[0], 0);
+  for (int kt = 0; kt + 1 < n_k; ++kt) stage(kt, std::false_type{});
+  stage(n_k - 1, std::true_type{});
 
-  // ---- epilogue: lane = token, registers = consecutive output rows --------
+  // ---- epilogue --------------------------------------------------------------
+  // A wave's rows come in units of 64 (one head of 64 dims, or half of one of
+  // 128): a unit is all q, all k or all v, of one head.  Lane = token and
+  // registers = consecutive rows in the accumulators; the unit is rotated and
+  // rounded there, then passed through the wave's own LDS region so that every
+  // lane stores 16 contiguous bytes: 8 dims of one token (q, k) or 8 tokens of
+  // one dim (v, stored dim-major).
+  __syncthreads();                                     // the LDS stages are free
   const int HD = a.heads * D;
+  const int tok_w = t0 + kWaveToks * tw;               // first token of the wave's columns
+  uint16_t* E = reinterpret_cast<uint16_t*>(&lds[0][0]) + wave * kEpiWaveElems;
 #pragma unroll
-  for (int cb = 0; cb < kRB; ++cb) {
-    const int chb = ch0 + kWaveRows * cw + 32 * cb;   // first row of this 32-row block
-    if (chb >= a.n_ch) continue;
-    const int which = chb / HD;                        // 0 q, 1 k, 2 v (a 32-row block never straddles)
-    const int rem = chb - which * HD;
-    const int h = rem / D;
-    const int d0 = rem - h * D;                        // first dim of the block within the head
+  for (int u = 0; u < kWaveRows / 64; ++u) {
+    const int r0 = ch0 + kWaveRows * cw + 64 * u;      // first row of the unit
+    if (r0 >= a.n_ch) break;                           // n_ch is a multiple of 64
+    const int which = r0 / HD;                         // 0 q, 1 k, 2 v
+    const int h = (r0 - which * HD) / D;
+    const int dbase = r0 - which * HD - h * D;         // 0, or 64 in a 128-dim head
+    if (which == 0 && a.q == nullptr) continue;
+    const bool rotate = which < 2 && a.rope != nullptr;
 #pragma unroll
-    for (int tb = 0; tb < kTB; ++tb) {
-      const int tok = t0 + kWaveToks * tw + 32 * tb + (lane & 31);
-      const bool valid = tok < a.n_tokens;
-      f32x16 y = acc[cb][tb];
-      if (which < 2 && a.rope != nullptr && valid) {
-        // pairs (d, d + 1), d even: registers (i, i + 1) with i even
+    for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const int d = d0 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const float2 cs = *reinterpret_cast<const float2*>(a.rope + ((int64_t)tok * (D / 2) + d / 2) * 2);
-          const float y0 = y[i], y1 = y[i + 1];
-          y[i] = y0 * cs.x - y1 * cs.y;
-          y[i + 1] = y0 * cs.y + y1 * cs.x;
+      for (int tb = 0; tb < kTB; ++tb) {
+        const int tl = 32 * tb + (lane & 31);          // token within the wave's columns
+        const int tok = tok_w + tl;
+        const bool valid = tok < a.n_tokens;
+        f32x16 y = acc[2 * u + c2][tb];
+        if (rotate && valid) {
+          // pairs (d, d + 1), d even: registers (i, i + 1), i even; the table
+          // is pair-major, so the lanes (consecutive tokens) read one run
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const int d = dbase + 32 * c2 + 8 * (i >> 2) + 4 * half + (i & 3);
+            const float2 cs = *reinterpret_cast<const float2*>(a.rope + ((int64_t)(d >> 1) * a.n_tokens + tok) * 2);
+            const float y0 = y[i], y1 = y[i + 1];
+            y[i] = y0 * cs.x - y1 * cs.y;
+            y[i + 1] = y0 * cs.y + y1 * cs.x;
+          }
         }
-      }
-      if (!valid) {
+        if (!valid) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = 0.f;         // the slot's tail reads as zeros
-      }
-      if (which == 0) {
-        if (!valid || a.q == nullptr) continue;
-        uint16_t* qp = a.q + ((int64_t)tok * a.heads + h) * D;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = d0 + 8 * g + 4 * half;
-          uint2 v;
-          v.x = pack2(y[4 * g], y[4 * g + 1]);
-          v.y = pack2(y[4 * g + 2], y[4 * g + 3]);
-          *reinterpret_cast<uint2*>(qp + d) = v;
+          for (int i = 0; i < 16; ++i) y[i] = 0.f;       // the slot's tail reads as zeros
         }
-      } else if (tok < a.t_pad) {
-        const int64_t mat = (int64_t)a.t_pad * D;
-        uint16_t* base = a.ring + ((int64_t)(a.slot * 2 + which - 1) * a.heads + h) * mat;
-        if (which == 1) {           // K: token-major [T_pad][D]
+        if (which < 2) {               // E: [token][64 dims], pitch kEpiTokPitch
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int d = d0 + 8 * g + 4 * half;
             uint2 v;
             v.x = pack2(y[4 * g], y[4 * g + 1]);
             v.y = pack2(y[4 * g + 2], y[4 * g + 3]);
-            *reinterpret_cast<uint2*>(base + (int64_t)tok * D + d) = v;
+            *reinterpret_cast<uint2*>(E + tl * kEpiTokPitch + 32 * c2 + 8 * g + 4 * half) = v;
           }
-        } else {                    // V: dim-major [D][T_pad]
+        } else {                       // E: [64 dims][tokens], pitch kEpiDimPitch
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int d = d0 + 8 * (i >> 2) + 4 * half + (i & 3);
-            bf16x2 p;
-            p[0] = (__bf16)y[i];
-            base[(int64_t)d * a.t_pad + tok] = __builtin_bit_cast(uint16_t, p[0]);
+            bf16x2 pk;
+            pk[0] = (__bf16)y[i];
+            E[(32 * c2 + 8 * (i >> 2) + 4 * half + (i & 3)) * kEpiDimPitch + tl] = __builtin_bit_cast(uint16_t, pk[0]);
           }
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (which < 2) {
+      // 8 lanes per token (64 dims), 8 tokens per store instruction
+      uint16_t* base;
+      int64_t tstride;
+      int tlimit;
+      if (which == 0) {
+        base = a.q + (int64_t)h * D + dbase;
+        tstride = HD;
+        tlimit = a.n_tokens;
+      } else {
+        base = a.ring + ((int64_t)(a.slot * 2) * a.heads + h) * ((int64_t)a.t_pad * D) + dbase;
+        tstride = D;
+        tlimit = a.t_pad;
+      }
+#pragma unroll
+      for (int j = 0; j < kWaveToks / 8; ++j) {
+        const int tl = 8 * j + (lane >> 3);
+        const int tok = tok_w + tl;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(E + tl * kEpiTokPitch + 8 * (lane & 7));
+        if (tok < tlimit) *reinterpret_cast<u32x4*>(base + tok * tstride + 8 * (lane & 7)) = v;
+      }
+    } else {
+      // kWaveToks / 8 lanes per dim row, 8 tokens each
+      constexpr int kLanesPerRow = kWaveToks / 8;
+      constexpr int kRowsPerStore = 64 / kLanesPerRow;
+      uint16_t* base = a.ring + ((int64_t)(a.slot * 2 + 1) * a.heads + h) * ((int64_t)a.t_pad * D);
+      const int c = lane % kLanesPerRow;
+      const int tok = tok_w + 8 * c;                   // a multiple of 8: the 8 tokens share the bound
+#pragma unroll
+      for (int j = 0; j < 64 / kRowsPerStore; ++j) {
+        const int r = kRowsPerStore * j + lane / kLanesPerRow;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(E + r * kEpiDimPitch + 8 * c);
+        if (tok < a.t_pad) *reinterpret_cast<u32x4*>(base + (int64_t)(dbase + r) * a.t_pad + tok) = v;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
+
 
 }  // namespace
 
 hipError_t launch_project(const ProjArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid((a.t_pad + kProjTokTile - 1) / kProjTokTile,
-                  (a.n_ch - a.ch_begin + kProjChTile - 1) / kProjChTile);
+  const dim3 grid(((a.t_pad + kProjTokTile - 1) / kProjTokTile) *
+                  ((a.n_ch - a.ch_begin + kProjChTile - 1) / kProjChTile));
   if (head_dim == 64)
     hipLaunchKernelGGL(project_kernel<64>, grid, dim3(kThreads), 0, s, a);
   else

@@ -181,14 +181,17 @@ size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_b
  * ba_cache_append, tokens [n_tokens, T_pad) zeroed), and Q into q:
  *   Y = X W^T;  q | k | v = Y[:, 0:HD] | Y[:, HD:2HD] | Y[:, 2HD:3HD]  (HD = heads * head_dim)
  * then, if rope is given, every adjacent pair (y[2p], y[2p+1]) of q and k is
- * rotated by the table's (c, s) for its token: (y0 c - y1 s, y0 s + y1 c).
+ * rotated by the table's (c, s) for its token and pair: (y0 c - y1 s,
+ * y0 s + y1 c), the same for every head.
  * x:    [n_tokens][dim] bf16, 1 <= n_tokens <= cache->slot_tokens, dim a
  *       multiple of 64 (n_tokens * dim < 2^30).
  * w:    [3 * heads * head_dim][dim] bf16 (a linear layer's weight: output
  *       rows q, then k, then v, each head-major).
  * q:    [n_tokens][heads][head_dim] bf16, or NULL to skip the q rows.
  * cache: bf16 ring; heads and head_dim (64 or 128) give the shapes.
- * rope: [n_tokens][head_dim / 2][2] fp32 (cos, sin), 8-byte aligned, or NULL.
+ * rope: [head_dim / 2][n_tokens][2] fp32 (cos, sin) of pair p at token t at
+ *       element 2 (p n_tokens + t): pair-major, so that consecutive tokens
+ *       read one run; 8-byte aligned, or NULL.
  * Products accumulate in fp32 on the matrix cores; the rotation is fp32;
  * every output is rounded once to bf16 (nearest even).  Does not change
  * cache->appended.

@@ -41,8 +41,9 @@ def _case(L, dim, H, D, slot, n_slots, with_q, with_rope, seed):
         table = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
     ring = B.ba_ring_init(n_slots, L + 37, H, D, B.BA_BF16)
     q = torch.full((L, H, D), float("nan"), dtype=torch.bfloat16, device="cuda") if with_q else None
+    # the library takes the table pair-major: [D/2][L][2]
     B.ba_qkv_project(to_dev(x, "bf16"), to_dev(w, "bf16"), ring, slot, q=q,
-                     rope=torch.from_numpy(table).cuda() if with_rope else None)
+                     rope=torch.from_numpy(table.transpose(1, 0, 2).copy()).cuda() if with_rope else None)
     torch.cuda.synchronize()
     qe, ke, ve = P.qkv_project_ref(x, w, H, D, table)
     absx = np.abs(N.bf16_bits_to_f64(x))
