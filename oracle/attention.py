@@ -85,3 +85,33 @@ def block_attention_ref(q, ring, text_ring, metas, scale=None, heads=None, rows=
             out[b, r, h, :] = o
             lse[b, h, r] = l
     return out, lse
+
+
+def merge_partials(o1, lse1, o2, lse2):
+    """Attention over the union of two disjoint key sets, from each part's
+    normalised output o [..., Dv] and log-sum-exp lse [...]: a key's weight in
+    the union is its weight in its part times exp(lse_part - lse_union), with
+    lse_union = log(exp(lse1) + exp(lse2)).  fp64."""
+    o1, o2 = np.asarray(o1, np.float64), np.asarray(o2, np.float64)
+    l1, l2 = np.asarray(lse1, np.float64), np.asarray(lse2, np.float64)
+    with np.errstate(invalid="ignore"):             # rows not computed stay NaN
+        lse = np.logaddexp(l1, l2)
+        w1 = np.exp(l1 - lse)[..., None]
+        w2 = np.exp(l2 - lse)[..., None]
+    return w1 * o1 + w2 * o2, lse
+
+
+def split_text_attention_ref(q, ring, text_ring, metas, scale=None, heads=None, rows=None):
+    """Separate text cross-attention (Wan-style, the alternative to the joint
+    key set): the cache segments form one softmax (self-attention), the text
+    keys another (cross-attention), each normalised on its own.  Returns
+    ((o_self, lse_self), (o_text, lse_text)) in block_attention_ref's layout;
+    a block with no cache segments (or no text) gives NaN for that part."""
+    self_m = [dict(m, text_len=0) for m in metas]
+    text_m = [dict(m, segs=[]) for m in metas]
+    res = []
+    for ms in (self_m, text_m):
+        ok = [bool(sum(n for _, n in m["segs"]) + m.get("text_len", 0)) for m in ms]
+        safe = [m if g else dict(m, q_len=0) for m, g in zip(ms, ok)]
+        res.append(block_attention_ref(q, ring, text_ring, safe, scale=scale, heads=heads, rows=rows))
+    return tuple(res)

@@ -226,11 +226,61 @@ def pin_lse():
     assert np.allclose(lse, scipy.special.logsumexp(0.9 * q @ K.T, axis=1), atol=1e-12)
 
 
+def pin_split_text_parts_by_brute_force():
+    # separate text cross-attention: the self part is the 60-digit brute force
+    # over the cache segments alone, the text part over the text keys alone
+    rng, ring, tring, blocks, (tk, tv) = _tiny_ring_setup(seed=11)
+    H, D = 2, 4
+    q = rng.standard_normal((1, 5, H, D))
+    meta = {"q_len": 5, "segs": [(1, 5), (2, 6)], "text_slot": 0, "text_len": 3}
+    (os_, ls), (ot, lt) = A.split_text_attention_ref(q, ring, tring, [meta], scale=0.7)
+    for h in range(H):
+        Ks = np.concatenate([blocks[1][0][:, h], blocks[2][0][:, h]]).astype(np.float64)
+        Vs = np.concatenate([blocks[1][1][:, h], blocks[2][1][:, h]]).astype(np.float64)
+        ob, lb = brute_force_attention(q[0, :, h].tolist(), Ks.tolist(), Vs.tolist(), 0.7)
+        assert np.allclose(os_[0, :, h], ob, atol=1e-12) and np.allclose(ls[0, h], lb, atol=1e-12)
+        ob, lb = brute_force_attention(q[0, :, h].tolist(), tk[:, h].astype(np.float64).tolist(),
+                                       tv[:, h].astype(np.float64).tolist(), 0.7)
+        assert np.allclose(ot[0, :, h], ob, atol=1e-12) and np.allclose(lt[0, h], lb, atol=1e-12)
+
+
+def pin_split_parts_merge_to_joint():
+    # the two parts, weighted by exp(lse_part - lse_union), are the joint
+    # softmax over [cache | text] computed in one go; and the union's lse is
+    # the joint lse
+    rng, ring, tring, blocks, (tk, tv) = _tiny_ring_setup(seed=12)
+    H, D = 2, 4
+    q = rng.standard_normal((2, 6, H, D)) * 1.5
+    metas = [{"q_len": 6, "segs": [(0, 6), (3, 4)], "text_slot": 0, "text_len": 3},
+             {"q_len": 4, "segs": [(2, 6)], "text_slot": 0, "text_len": 1}]
+    joint, jl = A.block_attention_ref(q, ring, tring, metas)
+    (os_, ls), (ot, lt) = A.split_text_attention_ref(q, ring, tring, metas)
+    lt_rows = np.transpose(lt, (0, 2, 1))               # [b][row][head]
+    ls_rows = np.transpose(ls, (0, 2, 1))
+    merged, ml = A.merge_partials(os_, ls_rows, ot, lt_rows)
+    ok = ~np.isnan(joint)
+    assert np.allclose(merged[ok], joint[ok], rtol=0, atol=1e-12)
+    assert np.allclose(np.transpose(ml, (0, 2, 1))[~np.isnan(jl)], jl[~np.isnan(jl)], atol=1e-12)
+    # the parts differ from the joint output (the text competes in the joint softmax)
+    assert np.abs(os_[ok] - joint[ok]).max() > 1e-3
+
+
+def pin_merge_partials_closed_form():
+    # two single-key parts: the union is the two-key softmax, a logistic mix
+    v1, v2 = np.array([1.0, -2.0]), np.array([3.0, 0.5])
+    for s1, s2 in [(0.3, -1.1), (5.0, 5.0), (-40.0, 2.0)]:
+        o, l = A.merge_partials(v1[None], np.array([s1]), v2[None], np.array([s2]))
+        w = 1.0 / (1.0 + math.exp(s2 - s1))
+        assert np.allclose(o[0], w * v1 + (1 - w) * v2, atol=1e-15)
+        assert abs(l[0] - (max(s1, s2) + math.log1p(math.exp(-abs(s1 - s2))))) < 1e-14
+
+
 ATTENTION_PINS = [pin_brute_force, pin_two_key_closed_form, pin_weights_sum_to_one,
                   pin_key_permutation_invariance, pin_uniform_when_q_zero, pin_needle,
                   pin_full_prefix_equivalence, pin_key_set_order_and_lengths,
                   pin_tokens_past_length_ignored, pin_default_scale,
-                  pin_rows_and_heads_subset, pin_lse]
+                  pin_rows_and_heads_subset, pin_lse, pin_split_text_parts_by_brute_force,
+                  pin_split_parts_merge_to_joint, pin_merge_partials_closed_form]
 
 
 # ---------------------------------------------------------------------------
@@ -748,6 +798,23 @@ def _mut_projection_weight_not_transposed(orig):
     return qkv_project_ref
 
 
+def _mut_merge_weights_swapped(orig):
+    def merge_partials(o1, lse1, o2, lse2):
+        l1, l2 = np.asarray(lse1, np.float64), np.asarray(lse2, np.float64)
+        with np.errstate(invalid="ignore"):
+            lse = np.logaddexp(l1, l2)
+            return np.exp(l2 - lse)[..., None] * o1 + np.exp(l1 - lse)[..., None] * o2, lse
+    return merge_partials
+
+
+def _mut_split_text_keeps_cache(orig):
+    def split_text_attention_ref(q, ring, text_ring, metas, scale=None, heads=None, rows=None):
+        self_m = [dict(m, text_len=0) for m in metas]
+        return (A.block_attention_ref(q, ring, text_ring, self_m, scale, heads, rows),
+                A.block_attention_ref(q, ring, text_ring, metas, scale, heads, rows))
+    return split_text_attention_ref
+
+
 MUTATIONS = [
     (A, "key_set", _mut_drop_text),
     (A, "key_set", _mut_seg_off_by_one),
@@ -767,6 +834,8 @@ MUTATIONS = [
     (Q, "plan", _mut_queue_single_buffer),
     (P, "rotate_pairs", _mut_rotation_sign),
     (P, "qkv_project_ref", _mut_projection_weight_not_transposed),
+    (A, "merge_partials", _mut_merge_weights_swapped),
+    (A, "split_text_attention_ref", _mut_split_text_keeps_cache),
 ]
 
 
