@@ -228,6 +228,67 @@ def project_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def cross_bench(args):
+    """One JSON line for the separate text cross-attention at the 480p
+    block's shape: 5400 queries, 24 heads x 64, a 512-token text (a padded
+    prompt), no cache segments; beside it the self part alone (cache
+    [5400 | 5400], no text) and the joint call over [cache | text]."""
+    import torch
+    import block_wise_long_amd as B
+    torch.cuda.set_device(0)
+    L, H, D, TXT = 5400, 24, 64, 512
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20256)
+
+    def rnd(*shape):
+        return (torch.randn(shape, device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
+    ring = B.ba_ring_init(2, L, H, D, B.BA_BF16)
+    B.ba_cache_append_batched(ring, rnd(2, L, H, D), rnd(2, L, H, D), [0, 1])
+    text = B.ba_ring_init(1, TXT, H, D, B.BA_BF16)
+    B.ba_cache_append(text, rnd(TXT, H, D), rnd(TXT, H, D), TXT)
+    q = rnd(1, L, H, D)
+    out = torch.empty_like(q)
+    segs = [(0, L), (1, L)]
+    m_cross = [B.make_meta(L, [], 0, TXT)]
+    m_self = [B.make_meta(L, segs, 0, 0)]
+    m_joint = [B.make_meta(L, segs, 0, TXT)]
+    stream = torch.cuda.current_stream()
+
+    def timed(metas):
+        for _ in range(max(args.warmup, 1)):
+            B.ba_block_attention(q, ring, text, metas, out=out)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            B.ba_block_attention(q, ring, text, metas, out=out)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    ms_cross = timed(m_cross)
+    ms_self = timed(m_self)
+    ms_joint = timed(m_joint)
+    flops = 4.0 * L * TXT * D * H
+    tf = flops / (ms_cross * 1e-3) / 1e12
+    res = {"metric": "separate text cross-attention TFLOP/s at 1 GPU",
+           "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_cross, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "text-cross-attention-480p-block", "queries": L, "heads": H, "head_dim": D,
+                      "text_keys": TXT},
+           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "kernel": f"attention_bf16_kernel<{D}>", "flop_per_launch": flops},
+           # q and out cross HBM once each; text K/V are 3 MB
+           "hbm_bytes_per_launch": 2 * L * H * D * 2 + 2 * TXT * H * D * 2,
+           "self_only_ms": round(ms_self, 5),
+           "split_ms": round(ms_self + ms_cross, 5),
+           "joint_ms": round(ms_joint, 5)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,11 +300,19 @@ def main():
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--queue", action="store_true",
                     help="time the single-GPU FIFO queue step (8 blocks of the 480p shape) instead")
+    ap.add_argument("--cross", action="store_true",
+                    help="time the separate text cross-attention (480p block, 512 text keys) instead")
     ap.add_argument("--project", action="store_true",
                     help="time the fused K/V producer (QKV projection of the 480p block) instead")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.cross:
+        if args.gpus != 1:
+            print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+            sys.exit(2)
+        cross_bench(args)
         return
     if args.project:
         if args.gpus != 1:

@@ -75,6 +75,8 @@ _SIGS = {
                                   ctypes.POINTER(ba_block_meta), _I32, ctypes.c_float, _P, _P,
                                   _P, ctypes.c_size_t, _P]),
     "ba_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
+    "ba_attention_plan": (_I32, [_I32, ctypes.POINTER(ba_ring), ctypes.POINTER(ba_ring),
+                                 ctypes.POINTER(ba_block_meta), _I32, ctypes.c_size_t, ctypes.POINTER(_I32)]),
     "ba_block_update": (_I32, [_P, _P, _I64, ctypes.POINTER(_I32), _I32, ctypes.POINTER(ba_schedule), _P]),
     "ba_schedule_coefficients": (_I32, [ctypes.POINTER(ba_schedule), ctypes.POINTER(_I32), _I32,
                                         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
@@ -222,6 +224,21 @@ def make_meta(q_len, segs, text_slot=0, text_len=0):
     for i, (s, n) in enumerate(segs):
         m.seg[i].slot, m.seg[i].len = s, n
     return m
+
+
+def ba_attention_plan(q_stride, cache, text, metas, workspace_bytes):
+    """Tail workgroups per XCD the attention call would use with a workspace
+    of workspace_bytes (0: whole query tiles per workgroup); launches nothing."""
+    nb = len(metas)
+    arr = (ba_block_meta * max(nb, 1))()
+    for i, m in enumerate(metas):
+        arr[i] = m if isinstance(m, ba_block_meta) else make_meta(
+            m["q_len"], m["segs"], m.get("text_slot", 0), m.get("text_len", 0))
+    tail = ctypes.c_int32(-1)
+    _check(_lib.ba_attention_plan(q_stride, ctypes.byref(cache.desc),
+                                  ctypes.byref(text.desc) if text is not None else None,
+                                  arr, nb, workspace_bytes, ctypes.byref(tail)), "ba_attention_plan")
+    return tail.value
 
 
 def ba_attention_workspace_bytes(head_dim, dtype, n_blocks, q_stride, heads):

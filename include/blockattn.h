@@ -153,6 +153,9 @@ typedef struct {
  *          evenly over the workgroups the device holds at once; the pieces of
  *          a cut task are written there and folded by a second kernel on the
  *          same stream.  Without it (NULL) each query tile is one workgroup.
+ *          The split is skipped when the pieces would be short (fewer than
+ *          24 key tiles of 64 per tail workgroup, e.g. a text-only key set);
+ *          ba_attention_plan tells which schedule a call takes.
  *          Results agree to rounding either way and are deterministic.  Its
  *          contents need no initialisation; calls that share a workspace must
  *          be ordered on one stream.
@@ -172,6 +175,16 @@ ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cac
  * sharing the split. */
 size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_blocks,
                                     int32_t q_stride, int32_t heads);
+
+/* The schedule ba_block_attention would take for these arguments and a
+ * workspace of workspace_bytes (0: none), without launching anything:
+ * *tail_workgroups = tail workgroups per XCD sharing the split (the largest
+ * over the call's launches of 16 blocks), 0 when every workgroup runs whole
+ * query tiles.  Same argument checks as ba_block_attention; with a workspace
+ * and a bf16 ring it queries the current device. */
+ba_status ba_attention_plan(int32_t q_stride, const ba_ring* cache, const ba_ring* text,
+                            const ba_block_meta* meta, int32_t n_blocks, size_t workspace_bytes,
+                            int32_t* tail_workgroups);
 
 /*
  * Fused K/V producer: the QKV projection of one block, written where it is

@@ -21,7 +21,7 @@ FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dere
 
 def test_exports_every_declared_symbol():
     names = B.header_symbols()
-    assert len(names) == 16
+    assert len(names) == 17
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -175,6 +175,25 @@ def test_attention_rejects():
     assert "head_dim" in B.ba_last_error()
     assert _attn(c, None, [_meta()], ws=FAKE + 64, ws_bytes=1 << 20) == B.BA_ERR_INVALID_ARG
     assert "workspace" in B.ba_last_error()
+
+
+def test_attention_plan_on_the_host():
+    # no workspace: whole query tiles, decided without a device; the same
+    # argument checks as the attention call
+    c, t = _ring(), _ring(1, 30)
+    tail = ctypes.c_int32(-1)
+
+    def plan(cache, text, metas, q_stride=16, ws_bytes=0, out=ctypes.byref(tail)):
+        arr = (B.ba_block_meta * len(metas))(*metas)
+        return B.raw.ba_attention_plan(q_stride, ctypes.byref(cache) if cache is not None else None,
+                                       ctypes.byref(text) if text is not None else None,
+                                       arr, len(metas), ws_bytes, out)
+    assert plan(c, t, [_meta(text_len=3)]) == B.BA_OK and tail.value == 0
+    assert plan(c, None, [_meta(segs=((2, 5),))]) == B.BA_ERR_OUT_OF_RANGE
+    assert plan(c, None, [_meta(text_len=3)]) == B.BA_ERR_INVALID_ARG
+    assert plan(None, None, [_meta()]) == B.BA_ERR_INVALID_ARG
+    assert plan(c, None, [_meta()], q_stride=0) == B.BA_ERR_INVALID_ARG
+    assert plan(c, None, [_meta()], out=None) == B.BA_ERR_INVALID_ARG
 
 
 def test_workspace_bytes_without_device():
