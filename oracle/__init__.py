@@ -24,12 +24,17 @@ Sources (cited by page title and section):
 
 Modules:
   numerics   exact bf16 <-> fp64 conversion (own implementation)
-  attention  softmax(QK^T * scale) V over the [cache segments | text] key set
+  attention  softmax(QK^T * scale) V over the [cache segments | text] key set,
+             and the separate text cross-attention (two softmaxes) with the
+             merge of two disjoint key sets' results
   ring       byte-level model of the K/V ring buffer's documented layout
   schedule   DDPM linear betas, alpha-bar table, DDIM (eta = 0) block update,
              and the flow-matching (rectified flow, Euler) variant
   queue      the single-GPU FIFO block queue: which ring slots a step writes
              and reads, and each block's timestep
   projection the fused K/V producer: QKV projection and the pair rotation
+  noise      coordinated noise initialisation: shuffled assignment of a shared
+             noise pool's frames to each new block (SplitMix64, partial
+             Fisher-Yates) and the frame gather
 """
-from . import numerics, attention, ring, schedule, queue, projection  # noqa: F401
+from . import numerics, attention, ring, schedule, queue, projection, noise  # noqa: F401

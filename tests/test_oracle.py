@@ -18,6 +18,7 @@ import torch
 
 import oracle
 from oracle import attention as A
+from oracle import noise as NZ
 from oracle import numerics as N
 from oracle import ring as R
 from oracle import projection as P
@@ -634,7 +635,109 @@ def pin_rotation_relative_position():
 PROJECTION_PINS = [pin_projection_brute_force, pin_rotation_identity_quarter_turn_and_norm,
                    pin_rotation_relative_position]
 
-ALL_PINS = ATTENTION_PINS + RING_PINS + SCHEDULE_PINS + QUEUE_PINS + PROJECTION_PINS
+# ---------------------------------------------------------------------------
+# coordinated noise initialisation pins
+# ---------------------------------------------------------------------------
+
+def pin_noise_weyl_sequence():
+    # the generator is a Weyl sequence under a fixed finaliser: its k-th
+    # output is the finaliser of seed + (k + 1) gamma, whatever came before
+    for seed in (0, 1, 0xFFFFFFFFFFFFFFFF, 0x0123456789ABCDEF):
+        g = NZ.SplitMix64(seed)
+        for k in range(50):
+            assert g.next() == NZ.finalise((seed + (k + 1) * NZ.GAMMA) % (1 << 64))
+    # the finaliser is a bijection of 64-bit words: undo it step by step
+    inv1 = pow(0xBF58476D1CE4E5B9, -1, 1 << 64)
+    inv2 = pow(0x94D049BB133111EB, -1, 1 << 64)
+
+    def unshift(z, k):
+        x = z
+        for _ in range(64 // k + 1):
+            x = z ^ (x >> k)
+        return x
+    rng = _rng(60)
+    for z in rng.integers(0, 1 << 63, 20, dtype=np.int64).tolist() + [0, 1, (1 << 64) - 1]:
+        y = NZ.finalise(z)
+        x = unshift(((unshift(y, 31) * inv2) % (1 << 64)), 27)
+        x = unshift((x * inv1) % (1 << 64), 30)
+        assert x == z
+
+
+def pin_noise_below_rejects_the_biased_zone():
+    class Feed(NZ.SplitMix64):
+        def __init__(self, vals):
+            self.vals = list(vals)
+
+        def next(self):
+            return self.vals.pop(0)
+    n = (1 << 63) + 1                      # 2^64 mod n = 2^63 - 1: about half the words are rejected
+    g = Feed([5, (1 << 63) - 2, (1 << 63) + 7])
+    assert g.below(n) == ((1 << 63) + 7) % n and not g.vals
+    g = Feed([0, 7])
+    assert g.below(1) == 0 and g.vals == [7]   # n = 1: nothing rejected
+    # range and balance of small bounds
+    g = NZ.SplitMix64(61)
+    draws = [g.below(3) for _ in range(30000)]
+    cnt = np.bincount(draws, minlength=3)
+    assert cnt.sum() == 30000 and len(cnt) == 3
+    chi2 = float(((cnt - 10000.0) ** 2 / 10000.0).sum())
+    assert chi2 < 30.0                      # 2 dof: p ~ 3e-7
+
+
+def pin_noise_assign_distinct_excluded_deterministic():
+    for seed in (0, 7, 12345):
+        for pool, excl, bf in ((21, 3, 4), (21, 0, 21), (9, 8, 1), (33, 5, 8)):
+            for b in range(0, 40, 7):
+                a = NZ.assign(seed, b, pool, excl, bf)
+                assert len(a) == bf and len(set(a)) == bf and all(0 <= f < pool - excl for f in a)
+                assert NZ.assign(seed, b, pool, excl, bf) == a     # any GPU computes the same
+    seqs = {tuple(NZ.assign(3, b, 21, 3, 4)) for b in range(60)}
+    assert len(seqs) > 50                   # consecutive blocks do not repeat one pattern
+    for bad in ((0, 0, 10, 3, 8), (0, 0, 10, 10, 1)):   # more frames than candidates; none left
+        try:
+            NZ.assign(*bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"assign{bad} accepted")
+
+
+def pin_noise_assign_uniform():
+    # every ordering of the candidates equally likely: 24 permutations of 4,
+    # and the 20 ordered pairs of 5 (partial shuffle); chi-square, p ~ 1e-6
+    perms = {}
+    for seed in range(12000):
+        for b in (0, 1):
+            t = tuple(NZ.assign(seed, b, 6, 2, 4))
+            perms[t] = perms.get(t, 0) + 1
+    assert len(perms) == 24
+    c = np.array(list(perms.values()), float)
+    assert float(((c - 1000.0) ** 2 / 1000.0).sum()) < 66.0
+    pairs = {}
+    for seed in range(20000):
+        t = tuple(NZ.assign(seed, 3, 5, 0, 2))
+        pairs[t] = pairs.get(t, 0) + 1
+    assert len(pairs) == 20
+    c = np.array(list(pairs.values()), float)
+    assert float(((c - 1000.0) ** 2 / 1000.0).sum()) < 60.0
+
+
+def pin_noise_block_gather_by_hand():
+    C, F, E = 3, 7, 5
+    pool = np.arange(C * F * E, dtype=np.int64).reshape(C, F, E)
+    frames = [6, 0, 3]
+    out = NZ.noise_block_ref(pool, C, F, frames)
+    assert out.shape == (C, 3, E)
+    for c in range(C):
+        for i, f in enumerate(frames):
+            for e in range(E):
+                assert out[c, i, e] == (c * F + f) * E + e
+
+
+NOISE_PINS = [pin_noise_weyl_sequence, pin_noise_below_rejects_the_biased_zone,
+              pin_noise_assign_distinct_excluded_deterministic, pin_noise_assign_uniform,
+              pin_noise_block_gather_by_hand]
+
+ALL_PINS = ATTENTION_PINS + RING_PINS + SCHEDULE_PINS + QUEUE_PINS + PROJECTION_PINS + NOISE_PINS
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -815,6 +918,38 @@ def _mut_split_text_keeps_cache(orig):
     return split_text_attention_ref
 
 
+def _mut_noise_sattolo(orig):
+    def assign(seed, block_id, pool_frames, n_exclude, block_frames):
+        m = pool_frames - n_exclude
+        g = NZ.block_generator(seed, block_id)
+        a = list(range(m))
+        for i in range(block_frames):
+            if i + 1 < m:
+                j = i + 1 + g.below(m - i - 1)
+                a[i], a[j] = a[j], a[i]
+        return a[:block_frames]
+    return assign
+
+
+def _mut_noise_no_exclusion(orig):
+    def assign(seed, block_id, pool_frames, n_exclude, block_frames):
+        return orig(seed, block_id, pool_frames, 0, block_frames)
+    return assign
+
+
+def _mut_noise_biased_below(orig):
+    def below(self, n):
+        return self.next() % n
+    return below
+
+
+def _mut_noise_gather_transposed(orig):
+    def noise_block_ref(pool, channels, pool_frames, frames):
+        p = np.asarray(pool).reshape(pool_frames, channels, -1)
+        return np.stack([np.stack([p[f, c] for f in frames]) for c in range(channels)])
+    return noise_block_ref
+
+
 MUTATIONS = [
     (A, "key_set", _mut_drop_text),
     (A, "key_set", _mut_seg_off_by_one),
@@ -836,6 +971,10 @@ MUTATIONS = [
     (P, "qkv_project_ref", _mut_projection_weight_not_transposed),
     (A, "merge_partials", _mut_merge_weights_swapped),
     (A, "split_text_attention_ref", _mut_split_text_keeps_cache),
+    (NZ, "assign", _mut_noise_sattolo),
+    (NZ, "assign", _mut_noise_no_exclusion),
+    (NZ.SplitMix64, "below", _mut_noise_biased_below),
+    (NZ, "noise_block_ref", _mut_noise_gather_transposed),
 ]
 
 
