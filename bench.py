@@ -37,21 +37,30 @@ ATTN_SRC = os.path.join(ROOT, "block_wise_long_amd", "csrc", "attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_d64_dit480p_traffic.md")
 
 
-def kernel_hash():
-    with open(ATTN_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# the producer's tile shape lives in internal.h: both files key its counters
+PROJ_SRC = (os.path.join(ROOT, "block_wise_long_amd", "csrc", "project.hip"),
+            os.path.join(ROOT, "block_wise_long_amd", "csrc", "internal.h"))
+PROJ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "project_d64_qkv480p_traffic.md")
 
 
-def traffic_from_profile(workload_name):
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when it is missing or was taken on another version of the kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+def kernel_hash(src=ATTN_SRC):
+    h = hashlib.sha256()
+    for path in ((src,) if isinstance(src, str) else src):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload_name, traffic_file=TRAFFIC_FILE, src=ATTN_SRC):
+    """HBM bytes per launch from a committed counter summary, or None when it
+    is missing or was taken on another version of the kernel's source."""
+    if not os.path.exists(traffic_file):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(traffic_file).read()
     m = re.search(r"kernel_sha256_16:\s*([0-9a-f]+)", text)
     w = re.search(r"workload:\s*(\S+)", text)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m and b and w) or m.group(1) != kernel_hash() or w.group(1) != workload_name:
+    if not (m and b and w) or m.group(1) != kernel_hash(src) or w.group(1) != workload_name:
         return None
     return float(b.group(1))
 
@@ -220,11 +229,82 @@ def project_bench(args):
            "config": {"workload": "qkv-producer-480p-block", "tokens": L, "dim": dim, "rows": 3 * H * D,
                       "heads": H, "head_dim": D, "rotation": True},
            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic_from_profile("qkv-producer-480p-block", PROJ_TRAFFIC_FILE, PROJ_SRC),
                         "kernel": f"project_kernel<{D}>", "flop_per_launch": flops},
            "append_ms_same_kv": round(ms_append, 5),
            "library_mm_ms": round(ms_lib, 5),
            "library_mm_tflops": round(flops / (ms_lib * 1e-3) / 1e12, 2)}
+    print(json.dumps(res), flush=True)
+
+
+def noise_bench(args):
+    """One JSON line for the coordinated noise initialisation: a new 480p
+    block's latents (16 channels x 4 frames of a 60 x 90 plane, bf16) gathered
+    from a 21-frame pool (last 3 excluded); beside it the queue's stand-in
+    block (5400 x 24 x 64) and a size sweep with the Infinity Cache flushed
+    between calls."""
+    import torch
+    import block_wise_long_amd as B
+    torch.cuda.set_device(0)
+
+    def timed(pool, frames, out, flush=None, reps=None):
+        """Median over single calls, each between two events on the launch
+        stream (launch latency included: a block's gather is a few
+        microseconds of kernel time); with a flush, the Infinity Cache is
+        overwritten before each call."""
+        reps = args.steps if reps is None else reps
+        for _ in range(max(args.warmup, 1)):
+            B.ba_noise_block(pool, frames, out)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            if flush is not None:
+                flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            B.ba_noise_block(pool, frames, out)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    C, F, E, excl, bf = 16, 21, 60 * 90, 3, 4
+    pool = torch.randn((C, F, E), device="cuda").to(torch.bfloat16)
+    out = torch.empty((C, bf, E), dtype=torch.bfloat16, device="cuda")
+    frames = B.ba_noise_assign(20257, 5, F, excl, bf)
+    ms = timed(pool, frames, out)
+    nbytes = 2.0 * out.numel() * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # the queue's stand-in block: 8.3 M elements as 16 x 4 frames of 129600
+    E2 = 5400 * 24 * 64 // (C * bf)
+    pool2 = torch.randn((C, F, E2), device="cuda").to(torch.bfloat16)
+    out2 = torch.empty((C, bf, E2), dtype=torch.bfloat16, device="cuda")
+    ms2 = timed(pool2, frames, out2)
+    del pool2, out2
+    sweep = []
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for mb in (16, 64, 256, 1024):
+        e = (mb << 20) // (2 * 2 * C * bf) // 8 * 8          # read + write = mb
+        p = torch.empty((C, F, e), dtype=torch.bfloat16, device="cuda").normal_()
+        o = torch.empty((C, bf, e), dtype=torch.bfloat16, device="cuda")
+        t = timed(p, frames, o, flush=flush, reps=5)
+        sweep.append({"MB": round(4.0 * o.numel() / 1e6, 1), "ms": round(t, 4),
+                      "GBs": round(4.0 * o.numel() / (t * 1e-3) / 1e9, 1)})
+        del p, o
+    del flush
+    res = {"metric": "noise-block gather GB/s (coordinated noise initialisation) at 1 GPU",
+           "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "noise-block-480p", "channels": C, "pool_frames": F, "n_exclude": excl,
+                      "block_frames": bf, "frame_elems": E},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                        "frac": round(gbs / 8000.0, 4), "traffic": None, "kernel": "noise_gather_kernel",
+                        "bytes_per_launch": nbytes},
+           "standin_block_ms": round(ms2, 5),
+           "standin_block_GBs": round(4.0 * C * bf * E2 / (ms2 * 1e-3) / 1e9, 1),
+           "sweep": sweep}
     print(json.dumps(res), flush=True)
 
 
@@ -300,6 +380,8 @@ def main():
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--queue", action="store_true",
                     help="time the single-GPU FIFO queue step (8 blocks of the 480p shape) instead")
+    ap.add_argument("--noise", action="store_true",
+                    help="time the noise-block gather (coordinated noise initialisation) instead")
     ap.add_argument("--cross", action="store_true",
                     help="time the separate text cross-attention (480p block, 512 text keys) instead")
     ap.add_argument("--project", action="store_true",
@@ -307,6 +389,12 @@ def main():
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.noise:
+        if args.gpus != 1:
+            print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+            sys.exit(2)
+        noise_bench(args)
         return
     if args.cross:
         if args.gpus != 1:

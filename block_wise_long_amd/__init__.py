@@ -86,6 +86,8 @@ _SIGS = {
     "ba_queue_plan": (_I32, [ctypes.POINTER(ba_queue), ctypes.POINTER(_I32), ctypes.POINTER(ba_block_meta),
                              ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "ba_queue_advance": (_I32, [ctypes.POINTER(ba_queue)]),
+    "ba_noise_assign": (_I32, [ctypes.c_uint64, _I64, _I32, _I32, _I32, ctypes.POINTER(_I32)]),
+    "ba_noise_block": (_I32, [_P, _I32, _I32, _I64, ctypes.POINTER(_I32), _I32, _P, _P]),
     "ba_status_string": (ctypes.c_char_p, [_I32]),
     "ba_last_error": (ctypes.c_char_p, []),
     "ba_version": (_I32, []),
@@ -384,3 +386,29 @@ def ba_qkv_project(x, w, cache, slot, q=None, rope=None):
                                _dev(q, "q") if q is not None else None, ctypes.byref(d), slot,
                                _dev(rope, "rope") if rope is not None else None, _stream()),
            "ba_qkv_project")
+
+
+BA_NOISE_MAX_FRAMES = 64
+
+
+def ba_noise_assign(seed, block_id, pool_frames, n_exclude, block_frames):
+    """Pool frames (a list of ints) block block_id takes; host only."""
+    arr = (_I32 * max(block_frames, 1))()
+    _check(_lib.ba_noise_assign(seed & (2 ** 64 - 1), block_id, pool_frames, n_exclude, block_frames, arr),
+           "ba_noise_assign")
+    return list(arr[:block_frames])
+
+
+def ba_noise_block(pool, frames, out):
+    """pool: [channels][pool_frames][...] device tensor; out: [channels]
+    [len(frames)][...] of the same element type and frame size."""
+    if pool.dim() < 3 or out.dim() < 3 or pool.shape[0] != out.shape[0] or out.shape[1] != len(frames) \
+            or pool.shape[2:] != out.shape[2:] or pool.dtype != out.dtype:
+        raise ValueError("pool [C][F_pool][...] and out [C][len(frames)][...] must match")
+    if not (pool.is_contiguous() and out.is_contiguous()):
+        raise ValueError("pool and out must be contiguous")
+    frame_bytes = pool[0, 0].numel() * pool.element_size()
+    arr = (_I32 * max(len(frames), 1))(*frames)
+    _check(_lib.ba_noise_block(_dev(pool, "pool"), pool.shape[0], pool.shape[1], frame_bytes, arr, len(frames),
+                               _dev(out, "out"), _stream()), "ba_noise_block")
+    return out

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libblockattn.so")
-SOURCES = ["api.cpp", "append.hip", "update.hip", "attention.hip", "project.hip"]
+SOURCES = ["api.cpp", "append.hip", "update.hip", "attention.hip", "project.hip", "noise.hip"]
 ARCH = os.environ.get("BA_OFFLOAD_ARCH", "gfx950")
 
 

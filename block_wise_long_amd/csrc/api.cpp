@@ -151,7 +151,7 @@ const char* ba_status_string(ba_status s) {
 
 const char* ba_last_error(void) { return g_err; }
 
-int32_t ba_version(void) { return 1 * 10000 + 1 * 100 + 0; }
+int32_t ba_version(void) { return 1 * 10000 + 2 * 100 + 0; }
 
 size_t ba_ring_bytes(int32_t n_slots, int32_t slot_tokens, int32_t heads, int32_t head_dim,
                      int32_t dtype) {
@@ -597,6 +597,97 @@ ba_status ba_qkv_project(const void* x, int32_t n_tokens, int32_t dim, const voi
   a.ch_begin = q ? 0 : cache->heads * cache->head_dim;
   hipError_t e = ba::launch_project(a, cache->head_dim, stream);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return ok();
+}
+
+}  // extern "C"
+
+// ---- coordinated noise initialisation -------------------------------------
+
+namespace {
+
+static_assert(ba::kNoiseMaxFrames == BA_NOISE_MAX_FRAMES, "kernarg frame table");
+
+// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): a Weyl sequence with
+// increment 0x9E3779B97F4A7C15 whose states pass through a 64-bit finaliser.
+struct Mix64 {
+  uint64_t state;
+  uint64_t next() {
+    uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+  // uniform in [0, n): words below 2^64 mod n are rejected (no modulo bias)
+  uint64_t below(uint64_t n) {
+    const uint64_t threshold = (0 - n) % n;
+    for (;;) {
+      const uint64_t r = next();
+      if (r >= threshold) return r % n;
+    }
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+ba_status ba_noise_assign(uint64_t seed, int64_t block_id, int32_t pool_frames, int32_t n_exclude,
+                          int32_t block_frames, int32_t* frames) {
+  if (frames == nullptr) return fail(BA_ERR_INVALID_ARG, "frames is NULL");
+  if (block_id < 0) return fail(BA_ERR_OUT_OF_RANGE, "block_id < 0");
+  if (pool_frames < 1 || n_exclude < 0 || n_exclude >= pool_frames)
+    return fail(BA_ERR_OUT_OF_RANGE, "need pool_frames >= 1 and 0 <= n_exclude < pool_frames");
+  const int32_t m = pool_frames - n_exclude;
+  if (block_frames < 1 || block_frames > m || block_frames > BA_NOISE_MAX_FRAMES)
+    return fail(BA_ERR_OUT_OF_RANGE, "block_frames %d outside [1, min(%d, %d)]", block_frames, m,
+                BA_NOISE_MAX_FRAMES);
+  // block b's seed: output b of the generator seeded with `seed`; the Weyl
+  // state after b + 1 steps is seed + (b + 1) * gamma
+  Mix64 root{seed + (uint64_t)block_id * 0x9E3779B97F4A7C15ull};
+  Mix64 g{root.next()};
+  std::vector<int32_t> a(m);
+  for (int32_t i = 0; i < m; ++i) a[i] = i;
+  for (int32_t i = 0; i < block_frames; ++i) {
+    const int32_t j = i + (int32_t)g.below((uint64_t)(m - i));
+    const int32_t t = a[i];
+    a[i] = a[j];
+    a[j] = t;
+  }
+  for (int32_t i = 0; i < block_frames; ++i) frames[i] = a[i];
+  return ok();
+}
+
+ba_status ba_noise_block(const void* pool, int32_t channels, int32_t pool_frames, int64_t frame_bytes,
+                         const int32_t* frames, int32_t block_frames, void* out, hipStream_t stream) {
+  if (pool == nullptr || out == nullptr || frames == nullptr)
+    return fail(BA_ERR_INVALID_ARG, "pool, out or frames is NULL");
+  if (!aligned(pool, 16) || !aligned(out, 16)) return fail(BA_ERR_INVALID_ARG, "pool or out not 16-byte aligned");
+  if (frame_bytes < 16 || frame_bytes % 16 != 0 || frame_bytes > ((int64_t)1 << 40))
+    return fail(BA_ERR_INVALID_ARG, "frame_bytes %lld must be a positive multiple of 16 (<= 2^40)",
+                (long long)frame_bytes);
+  if (channels < 1 || pool_frames < 1) return fail(BA_ERR_OUT_OF_RANGE, "channels and pool_frames must be >= 1");
+  if (block_frames < 1 || block_frames > BA_NOISE_MAX_FRAMES)
+    return fail(BA_ERR_OUT_OF_RANGE, "block_frames %d outside [1, %d]", block_frames, BA_NOISE_MAX_FRAMES);
+  if ((int64_t)channels * block_frames > 65535)
+    return fail(BA_ERR_OUT_OF_RANGE, "channels * block_frames > 65535");
+  for (int i = 0; i < block_frames; ++i)
+    if (frames[i] < 0 || frames[i] >= pool_frames)
+      return fail(BA_ERR_OUT_OF_RANGE, "frames[%d] = %d outside [0, %d)", i, frames[i], pool_frames);
+  const uintptr_t p0 = (uintptr_t)pool, p1 = p0 + (uintptr_t)channels * pool_frames * frame_bytes;
+  const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)channels * block_frames * frame_bytes;
+  if (o0 < p1 && p0 < o1) return fail(BA_ERR_INVALID_ARG, "out overlaps the pool");
+  ba::NoiseArgs a;
+  memset(&a, 0, sizeof(a));
+  a.pool = static_cast<const unsigned int __attribute__((ext_vector_type(4)))*>(pool);
+  a.out = static_cast<unsigned int __attribute__((ext_vector_type(4)))*>(out);
+  a.frame_vecs = frame_bytes / 16;
+  a.channels = channels;
+  a.pool_frames = pool_frames;
+  a.block_frames = block_frames;
+  for (int i = 0; i < block_frames; ++i) a.frames[i] = frames[i];
+  hipError_t e = ba::launch_noise(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "noise launch");
   return ok();
 }
 

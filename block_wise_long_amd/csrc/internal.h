@@ -165,6 +165,20 @@ constexpr int kProjTokTile = BA_PROJ_TOK;        // tokens per workgroup tile of
 constexpr int kProjChTile = BA_PROJ_CH;          // output rows per workgroup tile
 constexpr int kProjKStep = BA_PROJ_K;            // input dims per LDS stage
 
+// ---- coordinated noise initialisation ------------------------------------------
+constexpr int kNoiseMaxFrames = 64;      // frames per block (kernarg)
+struct NoiseArgs {
+  const unsigned int __attribute__((ext_vector_type(4)))* pool;   // [channels][pool_frames][frame_vecs]
+  unsigned int __attribute__((ext_vector_type(4)))* out;          // [channels][block_frames][frame_vecs]
+  int64_t frame_vecs;       // 16-byte vectors per frame
+  int32_t channels;
+  int32_t pool_frames;
+  int32_t block_frames;
+  int32_t pad_;
+  int32_t frames[kNoiseMaxFrames];
+};
+hipError_t launch_noise(const NoiseArgs& a, hipStream_t s);
+
 // ---- block update -----------------------------------------------------------
 struct UpdateArgs {
   uint16_t* x;              // [n_blocks][elems] bf16

@@ -17,16 +17,22 @@ and values, and the attention output is the prediction the update consumes
 import torch
 
 from . import (BA_BF16, ba_block_attention, ba_block_update, ba_cache_append, ba_cache_append_batched,
-               ba_queue_advance, ba_queue_init, ba_queue_plan, ba_queue_ring_slots, ba_ring_init)
+               ba_noise_assign, ba_noise_block, ba_queue_advance, ba_queue_init, ba_queue_plan,
+               ba_queue_ring_slots, ba_ring_init)
 
 
 class FifoQueue:
     """latents: [n_queue][tokens][heads][head_dim] bf16 on the GPU, latent
     slot m holding the block at queue position m (the head first) at
     timestep (m + 1) T / n_queue.  text_k, text_v: [text_len][heads][head_dim]
-    or None.  kind: "ddim" or "flow" (with shift)."""
+    or None.  kind: "ddim" or "flow" (with shift).  noise: optional dict
+    {"pool": [channels][pool_frames][...] bf16, "n_exclude": e, "seed": s}:
+    a step without a new block then draws the new tail block from the pool
+    (coordinated noise initialisation), its latents viewed as
+    [channels][block_frames][...] with the pool's frame size."""
 
-    def __init__(self, latents, text_k=None, text_v=None, T=1000, kind="ddim", shift=1.0, workspace="auto"):
+    def __init__(self, latents, text_k=None, text_v=None, T=1000, kind="ddim", shift=1.0, workspace="auto",
+                 noise=None):
         if latents.dtype != torch.bfloat16 or latents.dim() != 4:
             raise ValueError("latents must be [n_queue][tokens][heads][head_dim] bf16")
         n, L, H, D = latents.shape
@@ -41,16 +47,31 @@ class FifoQueue:
         self.pred = torch.empty_like(latents)
         self.T, self.kind, self.shift, self.workspace = T, kind, shift, workspace
         self.last_plan = None
+        self.noise = noise
+        if noise is not None:
+            pool = noise["pool"]
+            frame = pool[0, 0].numel()
+            per_block = L * H * D
+            if pool.dtype != torch.bfloat16 or per_block % (pool.shape[0] * frame):
+                raise ValueError("a block's latents must be a whole number of the pool's frames per channel")
+            self.block_frames = per_block // (pool.shape[0] * frame)
 
     @property
     def head_slot(self):
         """Latent slot of the current head block."""
         return self.q.head_id % self.q.n_queue
 
-    def step(self, new_block):
+    def new_block_frames(self):
+        """Pool frames of the block that enters at the next step."""
+        nz = self.noise
+        return ba_noise_assign(nz.get("seed", 0), self.q.head_id + self.q.n_queue, nz["pool"].shape[1],
+                               nz.get("n_exclude", 0), self.block_frames)
+
+    def step(self, new_block=None):
         """One queue step.  Returns the block that left the head (clean, a new
         tensor); new_block ([tokens][heads][head_dim] bf16, pure noise) takes
-        its latent slot as the new tail."""
+        its latent slot as the new tail, or, when None, the block is drawn
+        from the noise pool."""
         n = self.q.n_queue
         slots, metas, t, stride = ba_queue_plan(self.q)
         self.last_plan = (slots, metas, t, stride)
@@ -61,6 +82,13 @@ class FifoQueue:
                         {"kind": self.kind, "T": self.T, "stride": stride, "shift": self.shift})
         m = self.head_slot
         done = self.x[m].clone()
-        self.x[m].copy_(new_block)
+        if new_block is not None:
+            self.x[m].copy_(new_block)
+        else:
+            if self.noise is None:
+                raise ValueError("no new block and no noise pool")
+            pool = self.noise["pool"]
+            ba_noise_block(pool, self.new_block_frames(),
+                           self.x[m].view(pool.shape[0], self.block_frames, *pool.shape[2:]))
         ba_queue_advance(self.q)
         return done

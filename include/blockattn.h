@@ -320,6 +320,43 @@ ba_status ba_queue_plan(const ba_queue* q, int32_t* write_slots, ba_block_meta* 
  * advance by one. */
 ba_status ba_queue_advance(ba_queue* q);
 
+/*
+ * Coordinated noise initialisation.  Every GPU holds the same noise pool
+ * (DualParal Abstract: initial noise patterns shared across GPUs at no extra
+ * cost) and each new block takes its latent frames from the whole pool by a
+ * shuffled assignment that leaves out the pool's last few latents (the
+ * pith.science verdict on it, pith_inferences), so that concatenated blocks
+ * do not repeat one noise pattern.  The pool is the caller's (for instance
+ * N(0, 1) noise of the model's native clip length drawn from one seed).
+ */
+#define BA_NOISE_MAX_FRAMES 64
+
+/* (host only) The pool frames block `block_id` takes, in its frame order:
+ * block_frames distinct frames of [0, pool_frames - n_exclude), the first
+ * block_frames entries of a uniformly random permutation of those candidates
+ * (partial Fisher-Yates from the front: position i swaps with a uniform
+ * position in [i, m), m = pool_frames - n_exclude).  Random words come from
+ * SplitMix64 (Steele, Lea, Flood 2014: state += 0x9E3779B97F4A7C15, output
+ * the state through z ^= z >> 30, z *= 0xBF58476D1CE4E5B9, z ^= z >> 27,
+ * z *= 0x94D049BB133111EB, z ^= z >> 31); block b's generator is seeded with
+ * output b (0-based) of the generator seeded with `seed`, so each GPU computes
+ * any block's frames alone.  A uniform draw below n rejects words under
+ * 2^64 mod n and takes the rest mod n.  frames: block_frames int32 (host).
+ * Requires 0 <= n_exclude < pool_frames, 1 <= block_frames <=
+ * min(pool_frames - n_exclude, BA_NOISE_MAX_FRAMES), block_id >= 0. */
+ba_status ba_noise_assign(uint64_t seed, int64_t block_id, int32_t pool_frames, int32_t n_exclude,
+                          int32_t block_frames, int32_t* frames);
+
+/* The block's noise: out[c][f][:] = pool[c][frames[f]][:] for c < channels,
+ * f < block_frames (pool: [channels][pool_frames][frame_bytes] bytes, out:
+ * [channels][block_frames][frame_bytes]; any element type).  frames (host):
+ * block_frames entries in [0, pool_frames), e.g. from ba_noise_assign.
+ * pool and out 16-byte aligned, frame_bytes a positive multiple of 16,
+ * channels * block_frames <= 65535, block_frames <= BA_NOISE_MAX_FRAMES; out
+ * must not overlap the pool.  Enqueued on `stream`. */
+ba_status ba_noise_block(const void* pool, int32_t channels, int32_t pool_frames, int64_t frame_bytes,
+                         const int32_t* frames, int32_t block_frames, void* out, hipStream_t stream);
+
 const char* ba_status_string(ba_status status);
 const char* ba_last_error(void);
 int32_t     ba_version(void);   /* major*10000 + minor*100 + patch */

@@ -21,11 +21,11 @@ FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dere
 
 def test_exports_every_declared_symbol():
     names = B.header_symbols()
-    assert len(names) == 17
+    assert len(names) == 19
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert B.ba_version() == 10100
+    assert B.ba_version() == 10200
 
 
 @pytest.mark.parametrize("shape", [(2, 5400, 24, 64), (16, 5400, 24, 64), (2, 7800, 40, 128), (1, 226, 24, 64),
@@ -277,3 +277,34 @@ def test_project_rejects():
     assert f(FAKE, 100, 0, FAKE, FAKE, rr, 1, None, None) == B.BA_ERR_OUT_OF_RANGE
     r32 = _ring(n_slots=2, slot_tokens=100, heads=2, head_dim=64, dtype=B.BA_F32)
     assert f(FAKE, 100, 128, FAKE, FAKE, ctypes.byref(r32), 1, None, None) == B.BA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("pool,excl,bf", [(21, 3, 4), (21, 0, 21), (9, 8, 1), (64, 0, 64), (200, 17, 64), (5, 1, 3)])
+def test_noise_assign_matches_oracle(pool, excl, bf):
+    # the library's host bookkeeping and the oracle, from one published
+    # generator definition each: identical frame lists
+    from oracle import noise as NZ
+    for seed in (0, 1, 20251, 2 ** 64 - 1, 0x0123456789ABCDEF):
+        for b in (0, 1, 2, 7, 40, 999):
+            assert B.ba_noise_assign(seed, b, pool, excl, bf) == NZ.assign(seed, b, pool, excl, bf)
+
+
+def test_noise_rejects():
+    f = B.raw.ba_noise_assign
+    out = (ctypes.c_int32 * 64)()
+    assert f(0, 0, 10, 3, 8, out) == B.BA_ERR_OUT_OF_RANGE         # more frames than candidates
+    assert f(0, 0, 10, 10, 1, out) == B.BA_ERR_OUT_OF_RANGE        # no candidates
+    assert f(0, -1, 10, 0, 1, out) == B.BA_ERR_OUT_OF_RANGE
+    assert f(0, 0, 100, 0, 65, out) == B.BA_ERR_OUT_OF_RANGE       # kernarg table
+    assert f(0, 0, 10, 0, 0, out) == B.BA_ERR_OUT_OF_RANGE
+    assert f(0, 0, 10, 0, 1, None) == B.BA_ERR_INVALID_ARG
+    g = B.raw.ba_noise_block
+    fr = (ctypes.c_int32 * 2)(0, 3)
+    big = FAKE + (1 << 30)
+    assert g(FAKE, 2, 3, 64, fr, 2, big, None) == B.BA_ERR_OUT_OF_RANGE        # frame 3 >= pool_frames
+    assert g(FAKE, 2, 4, 40, fr, 2, big, None) == B.BA_ERR_INVALID_ARG         # frame bytes
+    assert g(FAKE + 8, 2, 4, 64, fr, 2, big, None) == B.BA_ERR_INVALID_ARG     # alignment
+    assert g(FAKE, 2, 4, 64, fr, 2, FAKE + 64, None) == B.BA_ERR_INVALID_ARG   # overlaps the pool
+    assert g(FAKE, 0, 4, 64, fr, 2, big, None) == B.BA_ERR_OUT_OF_RANGE
+    assert g(FAKE, 2000, 4, 64, fr, 64, big, None) == B.BA_ERR_OUT_OF_RANGE    # grid rows
+    assert g(None, 2, 4, 64, fr, 2, big, None) == B.BA_ERR_INVALID_ARG
