@@ -331,7 +331,7 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
     for (int m = 0; m < LA && m < NM; ++m) fr[m] = operand(m);
     bf16x8 pn[2];
     f32x16 s;
-    float la = 0.f, lb = 0.f;
+    float la, lb;
     // after MFMA m comes the share of the weight computation due by then
     int chunk = 0;
 #pragma unroll
@@ -353,7 +353,12 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
         pr[1] = (__bf16)e1;
         pn[k2][i] = pr[0];
         pn[k2][i + 1] = pr[1];
-        add_pair(e0, e1, la, lb);
+        if (chunk == 0) {        // the first pair starts the two chains (0 + x is not folded: -0)
+          la = e0;
+          lb = e1;
+        } else {
+          add_pair(e0, e1, la, lb);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
