@@ -125,7 +125,12 @@ template <> struct Shape<64> { static constexpr int NW = 4, WAVES_PER_SIMD = 3; 
 template <> struct Shape<128> { static constexpr int NW = 8, WAVES_PER_SIMD = 2; };
 
 constexpr int kBuffers = 3;   // LDS tile buffers: in use, being consumed, being filled
-constexpr int kLdsAhead = 2;  // a step's LDS operand reads issued ahead of their MFMA
+// a step's LDS operand reads issued ahead of their MFMA (D = 64: three waves
+// per SIMD hide the rest; D = 128: two waves, more reads in flight)
+#ifndef BA_LDS_AHEAD_128
+#define BA_LDS_AHEAD_128 3
+#endif
+template <int D> constexpr int kLdsAhead = D == 64 ? 2 : BA_LDS_AHEAD_128;
 
 template <int D>
 struct Tile {
@@ -314,7 +319,7 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
     using T = Tile<D>;
     constexpr int NKS = D / 16;
     constexpr int NM = NKS + 2 * NOB;           // MFMAs of the step
-    constexpr int LA = kLdsAhead;               // LDS reads in flight ahead of use
+    constexpr int LA = kLdsAhead<D>;            // LDS reads in flight ahead of use
     const int half = lane >> 5;
     const int r = 32 * gs + (lane & 31);
     // MFMA slot m: QK^T k-step m/2 on even slots while those last, PV
