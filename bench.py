@@ -156,7 +156,17 @@ def queue_bench(args):
     tk = (torch.randn((TXT, H, D), device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
     tv = (torch.randn((TXT, H, D), device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
     noise = (torch.randn((L, H, D), device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
-    fq = FifoQueue(lat, tk, tv, T=T)
+    layer = None
+    if args.layer:
+        # the layer through the fused K/V producer: random W, the usual
+        # rotation frequencies at positions 0..L-1 (pair-major table)
+        dim = H * D
+        w = (torch.randn((3 * dim, dim), device="cuda", generator=gen) * dim ** -0.5).to(torch.bfloat16)
+        pos = torch.arange(L, device="cuda", dtype=torch.float32)[:, None]
+        freq = 10000.0 ** (-torch.arange(D // 2, device="cuda", dtype=torch.float32) * 2 / D)[None, :]
+        ang = (pos * freq).t()
+        layer = {"w": w, "rope": torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).contiguous()}
+    fq = FifoQueue(lat, tk, tv, T=T, layer=layer)
     for _ in range(max(args.warmup, 1)):      # from step 1 on every block has its neighbour's context
         fq.step(noise)
     torch.cuda.synchronize()
@@ -173,8 +183,9 @@ def queue_bench(args):
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic",
-           "config": {"workload": "fifo-queue-8x480p", "n_queue": n, "block_tokens": L, "heads": H,
-                      "head_dim": D, "text": TXT, "T": T, "stride": T // n},
+           "config": {"workload": "fifo-queue-8x480p" + ("-qkv-layer" if args.layer else ""), "n_queue": n,
+                      "block_tokens": L, "heads": H, "head_dim": D, "text": TXT, "T": T, "stride": T // n,
+                      "layer": "qkv-projection (fused K/V producer)" if args.layer else "latents as q, k, v"},
            "tflops_step": round(flops / (ms * 1e-3) / 1e12, 2),
            "pct_bf16_peak_step": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
     print(json.dumps(res), flush=True)
@@ -215,6 +226,13 @@ def project_bench(args):
         return e0.elapsed_time(e1) / args.steps
 
     ms_proj = timed(lambda: B.ba_qkv_project(x, w, ring, 1, q=q, rope=rope))
+    # the 8 queued blocks of a FIFO step in one launch (43200 tokens)
+    nb = 8
+    xb = torch.randn((nb, L, dim), device="cuda", generator=gen).to(torch.bfloat16)
+    ringb = B.ba_ring_init(nb, L, H, D, B.BA_BF16)
+    qb = torch.empty((nb, L, H, D), dtype=torch.bfloat16, device="cuda")
+    ms_batch = timed(lambda: B.ba_qkv_project_batched(xb, w, ringb, list(range(nb)), q=qb, rope=rope))
+    del xb, ringb, qb
     ms_append = timed(lambda: B.ba_cache_append_batched(ring, k, k, [0]))
     # context only: the vendor library's linear layer on the same operands
     # (plain [tokens][rows] output, no rotation, no ring layout)
@@ -232,6 +250,8 @@ def project_bench(args):
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                         "traffic": traffic_from_profile("qkv-producer-480p-block", PROJ_TRAFFIC_FILE, PROJ_SRC),
                         "kernel": f"project_kernel<{D}>", "flop_per_launch": flops},
+           "batched_8_blocks_ms": round(ms_batch, 5),
+           "batched_8_blocks_tflops": round(8 * flops / (ms_batch * 1e-3) / 1e12, 2),
            "append_ms_same_kv": round(ms_append, 5),
            "library_mm_ms": round(ms_lib, 5),
            "library_mm_tflops": round(flops / (ms_lib * 1e-3) / 1e12, 2)}
@@ -380,6 +400,8 @@ def main():
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--queue", action="store_true",
                     help="time the single-GPU FIFO queue step (8 blocks of the 480p shape) instead")
+    ap.add_argument("--layer", action="store_true",
+                    help="with --queue: the layer's q, k, v come from the fused K/V producer")
     ap.add_argument("--noise", action="store_true",
                     help="time the noise-block gather (coordinated noise initialisation) instead")
     ap.add_argument("--cross", action="store_true",

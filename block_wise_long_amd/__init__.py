@@ -81,6 +81,8 @@ _SIGS = {
     "ba_schedule_coefficients": (_I32, [ctypes.POINTER(ba_schedule), ctypes.POINTER(_I32), _I32,
                                         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),
     "ba_qkv_project": (_I32, [_P, _I32, _I32, _P, _P, ctypes.POINTER(ba_ring), _I32, _P, _P]),
+    "ba_qkv_project_batched": (_I32, [_P, _I32, _I32, _I32, _P, _P, ctypes.POINTER(ba_ring), ctypes.POINTER(_I32),
+                                      _P, _I64, _P]),
     "ba_queue_init": (_I32, [ctypes.POINTER(ba_queue), _I32, _I32, _I32, _I32]),
     "ba_queue_ring_slots": (_I32, [_I32]),
     "ba_queue_plan": (_I32, [ctypes.POINTER(ba_queue), ctypes.POINTER(_I32), ctypes.POINTER(ba_block_meta),
@@ -386,6 +388,32 @@ def ba_qkv_project(x, w, cache, slot, q=None, rope=None):
                                _dev(q, "q") if q is not None else None, ctypes.byref(d), slot,
                                _dev(rope, "rope") if rope is not None else None, _stream()),
            "ba_qkv_project")
+
+
+def ba_qkv_project_batched(x, w, cache, slots, q=None, rope=None):
+    """x: [n_blocks][n_tokens][dim] bf16; block b's K/V go to ring slot
+    slots[b], its Q to q[b] ([n_blocks][n_tokens][heads][head_dim]) when q is
+    given.  rope: None, one [head_dim / 2][n_tokens][2] fp32 table for every
+    block, or [n_blocks][head_dim / 2][n_tokens][2]."""
+    if x.dim() != 3 or w.dim() != 2 or w.shape[1] != x.shape[2] or len(slots) != x.shape[0]:
+        raise ValueError("x must be [n_blocks][n_tokens][dim], w [3 * heads * head_dim][dim], one slot per block")
+    d = cache.desc
+    nb, L = x.shape[0], x.shape[1]
+    if w.shape[0] != 3 * d.heads * d.head_dim:
+        raise ValueError("w must have 3 * heads * head_dim rows")
+    if q is not None and q.numel() < nb * L * d.heads * d.head_dim:
+        raise ValueError("q too small")
+    stride = 0
+    if rope is not None:
+        table = L * d.head_dim
+        if rope.dtype != torch.float32 or rope.numel() not in (table, nb * table):
+            raise ValueError("rope must be fp32 [head_dim / 2][n_tokens][2] or [n_blocks][...]")
+        stride = table if rope.numel() == nb * table and nb > 1 else 0
+    arr = (_I32 * nb)(*slots)
+    _check(_lib.ba_qkv_project_batched(_dev(x, "x"), nb, L, x.shape[2], _dev(w, "w"),
+                                       _dev(q, "q") if q is not None else None, ctypes.byref(d), arr,
+                                       _dev(rope, "rope") if rope is not None else None, stride, _stream()),
+           "ba_qkv_project_batched")
 
 
 BA_NOISE_MAX_FRAMES = 64

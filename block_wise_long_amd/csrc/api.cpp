@@ -564,23 +564,34 @@ ba_status ba_queue_advance(ba_queue* q) {
 
 // ---- fused K/V producer -----------------------------------------------------
 
-ba_status ba_qkv_project(const void* x, int32_t n_tokens, int32_t dim, const void* w, void* q,
-                         const ba_ring* cache, int32_t slot, const float* rope, hipStream_t stream) {
+ba_status ba_qkv_project_batched(const void* x, int32_t n_blocks, int32_t n_tokens, int32_t dim, const void* w,
+                                 void* q, const ba_ring* cache, const int32_t* slots, const float* rope,
+                                 int64_t rope_block_stride, hipStream_t stream) {
   ba_status st = check_ring(cache, "cache");
   if (st != BA_OK) return st;
   if (cache->dtype != BA_BF16) return fail(BA_ERR_UNSUPPORTED, "the producer writes bf16 rings only");
-  if (x == nullptr || w == nullptr) return fail(BA_ERR_INVALID_ARG, "x or w is NULL");
+  if (x == nullptr || w == nullptr || slots == nullptr) return fail(BA_ERR_INVALID_ARG, "x, w or slots is NULL");
   if (!aligned(x, 16) || !aligned(w, 16) || (q && !aligned(q, 16)))
     return fail(BA_ERR_INVALID_ARG, "x, w or q not 16-byte aligned");
   if (rope && !aligned(rope, 8)) return fail(BA_ERR_INVALID_ARG, "rope not 8-byte aligned");
-  if (slot < 0 || slot >= cache->n_slots)
-    return fail(BA_ERR_OUT_OF_RANGE, "slot %d outside [0, %d)", slot, cache->n_slots);
+  if (n_blocks < 1 || n_blocks > ba::kProjMaxBlocks)
+    return fail(BA_ERR_OUT_OF_RANGE, "n_blocks %d outside [1, %d]", n_blocks, ba::kProjMaxBlocks);
+  for (int b = 0; b < n_blocks; ++b) {
+    if (slots[b] < 0 || slots[b] >= cache->n_slots)
+      return fail(BA_ERR_OUT_OF_RANGE, "slots[%d] = %d outside [0, %d)", b, slots[b], cache->n_slots);
+    for (int c = 0; c < b; ++c)
+      if (slots[c] == slots[b]) return fail(BA_ERR_INVALID_ARG, "blocks %d and %d share slot %d", c, b, slots[b]);
+  }
   if (n_tokens < 1 || n_tokens > cache->slot_tokens)
     return fail(BA_ERR_OUT_OF_RANGE, "n_tokens %d outside [1, %d]", n_tokens, cache->slot_tokens);
   if (dim < 64 || dim % 64 != 0 || (int64_t)n_tokens * dim >= ((int64_t)1 << 30))
     return fail(BA_ERR_OUT_OF_RANGE, "dim %d must be a positive multiple of 64 (n_tokens * dim < 2^30)", dim);
   const int64_t n_ch = 3 * (int64_t)cache->heads * cache->head_dim;
   if (n_ch * dim >= ((int64_t)1 << 30)) return fail(BA_ERR_OUT_OF_RANGE, "weight too large");
+  const int64_t table = (int64_t)n_tokens * cache->head_dim;   // floats of one block's table
+  if (rope && rope_block_stride != 0 && rope_block_stride < table)
+    return fail(BA_ERR_INVALID_ARG, "rope_block_stride %lld is neither 0 nor >= one table (%lld floats)",
+                (long long)rope_block_stride, (long long)table);
   ba::ProjArgs a;
   memset(&a, 0, sizeof(a));
   a.x = static_cast<const uint16_t*>(x);
@@ -588,16 +599,23 @@ ba_status ba_qkv_project(const void* x, int32_t n_tokens, int32_t dim, const voi
   a.q = static_cast<uint16_t*>(q);
   a.ring = static_cast<uint16_t*>(cache->base);
   a.rope = rope;
+  a.rope_bstride = rope ? rope_block_stride : 0;
   a.n_tokens = n_tokens;
   a.dim = dim;
   a.heads = cache->heads;
   a.t_pad = cache->slot_stride_tokens;
-  a.slot = slot;
   a.n_ch = (int32_t)n_ch;
   a.ch_begin = q ? 0 : cache->heads * cache->head_dim;
+  a.n_blocks = n_blocks;
+  for (int b = 0; b < n_blocks; ++b) a.slot[b] = slots[b];
   hipError_t e = ba::launch_project(a, cache->head_dim, stream);
   if (e != hipSuccess) return hip_fail(e, "projection launch");
   return ok();
+}
+
+ba_status ba_qkv_project(const void* x, int32_t n_tokens, int32_t dim, const void* w, void* q,
+                         const ba_ring* cache, int32_t slot, const float* rope, hipStream_t stream) {
+  return ba_qkv_project_batched(x, 1, n_tokens, dim, w, q, cache, &slot, rope, 0, stream);
 }
 
 }  // extern "C"

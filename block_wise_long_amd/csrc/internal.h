@@ -124,20 +124,23 @@ hipError_t attention_bf16_resident(int head_dim, int* per_cu);   // workgroups p
 int attention_f32_q_tile();
 
 // ---- fused K/V producer (QKV projection) --------------------------------------
+constexpr int kProjMaxBlocks = 64;       // blocks per producer launch (kernarg)
 struct ProjArgs {
-  const uint16_t* x;        // [n_tokens][dim] bf16
+  const uint16_t* x;        // [n_blocks][n_tokens][dim] bf16
   const uint16_t* w;        // [3 * heads * head_dim][dim] bf16 (rows q | k | v)
-  uint16_t* q;              // [n_tokens][heads][head_dim] bf16, or null (q rows skipped)
+  uint16_t* q;              // [n_blocks][n_tokens][heads][head_dim] bf16, or null (q rows skipped)
   uint16_t* ring;           // cache ring base
-  const float* rope;        // [n_tokens][head_dim / 2][2] (cos, sin), or null
+  const float* rope;        // [head_dim / 2][n_tokens][2] (cos, sin) per block, or null
+  int64_t rope_bstride;     // floats between blocks' tables (0: one table for all)
   int32_t n_tokens;
   int32_t dim;              // multiple of 64
   int32_t heads;
   int32_t t_pad;            // ring slot token stride
-  int32_t slot;             // ring slot K and V go to
   int32_t ch_begin;         // first output row computed: 0, or heads * head_dim without q
   int32_t n_ch;             // 3 * heads * head_dim
+  int32_t n_blocks;
   int32_t pad_;
+  int32_t slot[kProjMaxBlocks];   // ring slot of each block's K and V
 };
 hipError_t launch_project(const ProjArgs& a, int head_dim, hipStream_t s);
 #ifndef BA_PROJ_TOK

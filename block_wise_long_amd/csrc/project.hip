@@ -71,8 +71,8 @@ __device__ __forceinline__ unsigned pack2(float lo, float hi) {
 // from asm: no register result; the stage is read only after the vmcnt wait
 // and barrier that publish it).  Rows past the end are clamped to the last
 // row; their results are not stored.
-__device__ __forceinline__ void load_stage(const ProjArgs& a, int ch0, int t0, int k0, int tid,
-                                           unsigned stage_lds) {
+__device__ __forceinline__ void load_stage(const ProjArgs& a, const uint16_t* xb, int ch0, int t0, int k0,
+                                           int tid, unsigned stage_lds) {
   const int lane = tid & 63;
   const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);
 #pragma unroll
@@ -92,7 +92,7 @@ __device__ __forceinline__ void load_stage(const ProjArgs& a, int ch0, int t0, i
       const int r = q / kRowChunks, c = (q % kRowChunks) ^ swz(r);
       int tok = t0 + r;
       tok = tok < a.n_tokens ? tok : a.n_tokens - 1;
-      base = a.x;
+      base = xb;
       off = (unsigned)(tok * a.dim + k0 + 8 * c) * 2u;
     }
     const unsigned lds = stage_lds + 16u * (unsigned)p0;
@@ -133,17 +133,22 @@ static_assert(kStages >= 3 && kStages <= 7, "stages: the next stage is issued a 
 // kGroup token tiles channel tile by channel tile, so the workgroups resident
 // on one XCD at a time share most of their input rows and weight rows in
 // that XCD's L2.
+// Blocks of a batched call come one after the other in that order (they share
+// the weight rows).
 constexpr int kGroup = BA_PROJ_GROUP;
-struct TileXY { int tt, ct; };
-__device__ __forceinline__ TileXY tile_of(int w, int n_tt, int n_ct) {
-  const int n = n_tt * n_ct;
+struct TileXY { int b, tt, ct; };
+__device__ __forceinline__ TileXY tile_of(int w, int n_blocks, int n_tt, int n_ct) {
+  const int per_block = n_tt * n_ct;
+  const int n = n_blocks * per_block;
   const int x = w & 7, j = w >> 3;
   const int q = n >> 3, r = n & 7;
   const int rank = x * q + (x < r ? x : r) + j;     // this XCD's share starts at x*q + min(x, r)
-  const int band = rank / (kGroup * n_ct);
+  const int b = rank / per_block;
+  const int rb = rank - b * per_block;
+  const int band = rb / (kGroup * n_ct);
   const int g = min(kGroup, n_tt - band * kGroup);  // token tiles in this band
-  const int local = rank - band * kGroup * n_ct;
-  return {band * kGroup + local % g, local / g};
+  const int local = rb - band * kGroup * n_ct;
+  return {b, band * kGroup + local % g, local / g};
 }
 
 template <int D>
@@ -157,8 +162,13 @@ void project_kernel(const ProjArgs a) {
   const int wave = tid >> 6;
   const int cw = wave & 1;             // weight rows kWaveRows cw .. of the tile
   const int tw = wave >> 1;            // token rows kWaveToks tw .. of the tile (0 .. kWavesT - 1)
-  const TileXY tile = tile_of(blockIdx.x, (a.t_pad + kProjTokTile - 1) / kProjTokTile,
+  const TileXY tile = tile_of(blockIdx.x, a.n_blocks, (a.t_pad + kProjTokTile - 1) / kProjTokTile,
                               (a.n_ch - a.ch_begin + kProjChTile - 1) / kProjChTile);
+  // this tile's block: its input rows, q rows, rotation table and ring slot
+  const uint16_t* xb = a.x + (int64_t)tile.b * a.n_tokens * a.dim;
+  uint16_t* qb = a.q ? a.q + (int64_t)tile.b * a.n_tokens * a.heads * D : nullptr;
+  const float* ropeb = a.rope ? a.rope + (int64_t)tile.b * a.rope_bstride : nullptr;
+  const int slot = a.slot[tile.b];
   const int t0 = tile.tt * kProjTokTile;
   const int ch0 = a.ch_begin + tile.ct * kProjChTile;
   const int n_k = a.dim / kKStep;
@@ -178,7 +188,7 @@ void project_kernel(const ProjArgs a) {
   // so a wave's MFMA stream never waits on its own LDS reads.
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
-    if (s < n_k) load_stage(a, ch0, t0, s * kKStep, tid, lds_addr + 16u * kStageChunks * s);
+    if (s < n_k) load_stage(a, xb, ch0, t0, s * kKStep, tid, lds_addr + 16u * kStageChunks * s);
   {
     const int issued = n_k < kStages - 1 ? n_k : kStages - 1;
     wait_newer(issued - 1);                             // stage 0 has landed
@@ -214,7 +224,7 @@ void project_kernel(const ProjArgs a) {
         wait_newer((ahead < n_k ? ahead : n_k - 1) - (kt + 1));
         __syncthreads();
         if (kt + kStages - 1 < n_k)
-          load_stage(a, ch0, t0, (kt + kStages - 1) * kKStep, tid,
+          load_stage(a, xb, ch0, t0, (kt + kStages - 1) * kKStep, tid,
                      lds_addr + 16u * kStageChunks * ((kt + kStages - 1) % kStages));
         read_frag(nxt, lds[(kt + 1) % kStages], 0);
       }
@@ -249,8 +259,8 @@ void project_kernel(const ProjArgs a) {
     const int which = r0 / HD;                         // 0 q, 1 k, 2 v
     const int h = (r0 - which * HD) / D;
     const int dbase = r0 - which * HD - h * D;         // 0, or 64 in a 128-dim head
-    if (which == 0 && a.q == nullptr) continue;
-    const bool rotate = which < 2 && a.rope != nullptr;
+    if (which == 0 && qb == nullptr) continue;
+    const bool rotate = which < 2 && ropeb != nullptr;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
@@ -265,7 +275,7 @@ void project_kernel(const ProjArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
             const int d = dbase + 32 * c2 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const float2 cs = *reinterpret_cast<const float2*>(a.rope + ((int64_t)(d >> 1) * a.n_tokens + tok) * 2);
+            const float2 cs = *reinterpret_cast<const float2*>(ropeb + ((int64_t)(d >> 1) * a.n_tokens + tok) * 2);
             const float y0 = y[i], y1 = y[i + 1];
             y[i] = y0 * cs.x - y1 * cs.y;
             y[i + 1] = y0 * cs.y + y1 * cs.x;
@@ -302,11 +312,11 @@ void project_kernel(const ProjArgs a) {
       int64_t tstride;
       int tlimit;
       if (which == 0) {
-        base = a.q + (int64_t)h * D + dbase;
+        base = qb + (int64_t)h * D + dbase;
         tstride = HD;
         tlimit = a.n_tokens;
       } else {
-        base = a.ring + ((int64_t)(a.slot * 2) * a.heads + h) * ((int64_t)a.t_pad * D) + dbase;
+        base = a.ring + ((int64_t)(slot * 2) * a.heads + h) * ((int64_t)a.t_pad * D) + dbase;
         tstride = D;
         tlimit = a.t_pad;
       }
@@ -321,7 +331,7 @@ void project_kernel(const ProjArgs a) {
       // kWaveToks / 8 lanes per dim row, 8 tokens each
       constexpr int kLanesPerRow = kWaveToks / 8;
       constexpr int kRowsPerStore = 64 / kLanesPerRow;
-      uint16_t* base = a.ring + ((int64_t)(a.slot * 2 + 1) * a.heads + h) * ((int64_t)a.t_pad * D);
+      uint16_t* base = a.ring + ((int64_t)(slot * 2 + 1) * a.heads + h) * ((int64_t)a.t_pad * D);
       const int c = lane % kLanesPerRow;
       const int tok = tok_w + 8 * c;                   // a multiple of 8: the 8 tokens share the bound
 #pragma unroll
@@ -341,7 +351,7 @@ void project_kernel(const ProjArgs a) {
 }  // namespace
 
 hipError_t launch_project(const ProjArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid(((a.t_pad + kProjTokTile - 1) / kProjTokTile) *
+  const dim3 grid(a.n_blocks * ((a.t_pad + kProjTokTile - 1) / kProjTokTile) *
                   ((a.n_ch - a.ch_begin + kProjChTile - 1) / kProjChTile));
   if (head_dim == 64)
     hipLaunchKernelGGL(project_kernel<64>, grid, dim3(kThreads), 0, s, a);

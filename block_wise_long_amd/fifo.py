@@ -9,16 +9,21 @@ timestep) is the library's ba_queue_*; every step of the data path runs in
 the library's kernels: ba_cache_append_batched, ba_block_attention (one
 launch over all queued blocks), ba_block_update (each block at its own t).
 
-The model between those calls is a stand-in without trained weights: a
-block's latents, viewed as [tokens][heads][head_dim], are its queries, keys
-and values, and the attention output is the prediction the update consumes
-(the noise for DDIM, the velocity for flow matching).
+The model between those calls is a stand-in without trained weights.  By
+default a block's latents, viewed as [tokens][heads][head_dim], are its
+queries, keys and values.  With a projection layer (a weight W of
+[3 heads head_dim][heads head_dim], random in the tests and the bench, and an
+optional rotation table) every block's latents, viewed as [tokens][dim], go
+through one ba_qkv_project_batched launch instead, which writes K and V
+straight into each block's ring slot (no append) and Q to a buffer.  Either way the attention
+output is the prediction the update consumes (the noise for DDIM, the
+velocity for flow matching).
 """
 import torch
 
 from . import (BA_BF16, ba_block_attention, ba_block_update, ba_cache_append, ba_cache_append_batched,
-               ba_noise_assign, ba_noise_block, ba_queue_advance, ba_queue_init, ba_queue_plan,
-               ba_queue_ring_slots, ba_ring_init)
+               ba_noise_assign, ba_noise_block, ba_qkv_project_batched, ba_queue_advance, ba_queue_init,
+               ba_queue_plan, ba_queue_ring_slots, ba_ring_init)
 
 
 class FifoQueue:
@@ -29,10 +34,12 @@ class FifoQueue:
     {"pool": [channels][pool_frames][...] bf16, "n_exclude": e, "seed": s}:
     a step without a new block then draws the new tail block from the pool
     (coordinated noise initialisation), its latents viewed as
-    [channels][block_frames][...] with the pool's frame size."""
+    [channels][block_frames][...] with the pool's frame size.  layer:
+    optional dict {"w": [3 H D][H D] bf16, "rope": [D/2][tokens][2] fp32 or
+    None}: the QKV projection layer described above."""
 
     def __init__(self, latents, text_k=None, text_v=None, T=1000, kind="ddim", shift=1.0, workspace="auto",
-                 noise=None):
+                 noise=None, layer=None):
         if latents.dtype != torch.bfloat16 or latents.dim() != 4:
             raise ValueError("latents must be [n_queue][tokens][heads][head_dim] bf16")
         n, L, H, D = latents.shape
@@ -47,6 +54,12 @@ class FifoQueue:
         self.pred = torch.empty_like(latents)
         self.T, self.kind, self.shift, self.workspace = T, kind, shift, workspace
         self.last_plan = None
+        self.layer = layer
+        self.qbuf = None
+        if layer is not None:
+            if tuple(layer["w"].shape) != (3 * H * D, H * D) or layer["w"].dtype != torch.bfloat16:
+                raise ValueError("layer w must be [3 heads head_dim][heads head_dim] bf16")
+            self.qbuf = torch.empty_like(latents)
         self.noise = noise
         if noise is not None:
             pool = noise["pool"]
@@ -75,9 +88,16 @@ class FifoQueue:
         n = self.q.n_queue
         slots, metas, t, stride = ba_queue_plan(self.q)
         self.last_plan = (slots, metas, t, stride)
-        # the stand-in layer: keys and values are the latents themselves
-        ba_cache_append_batched(self.ring, self.x, self.x, slots)
-        ba_block_attention(self.x, self.ring, self.text, metas, out=self.pred, workspace=self.workspace)
+        if self.layer is None:
+            # keys and values are the latents themselves
+            ba_cache_append_batched(self.ring, self.x, self.x, slots)
+            q = self.x
+        else:
+            # one projection launch writes every block's K/V into its ring slot
+            ba_qkv_project_batched(self.x.view(n, self.x.shape[1], -1), self.layer["w"], self.ring, slots,
+                                   q=self.qbuf, rope=self.layer.get("rope"))
+            q = self.qbuf
+        ba_block_attention(q, self.ring, self.text, metas, out=self.pred, workspace=self.workspace)
         ba_block_update(self.x.view(n, -1), self.pred.view(n, -1), t,
                         {"kind": self.kind, "T": self.T, "stride": stride, "shift": self.shift})
         m = self.head_slot

@@ -212,6 +212,17 @@ ba_status ba_attention_plan(int32_t q_stride, const ba_ring* cache, const ba_rin
 ba_status ba_qkv_project(const void* x, int32_t n_tokens, int32_t dim, const void* w, void* q,
                          const ba_ring* cache, int32_t slot, const float* rope, hipStream_t stream);
 
+/* The same for n_blocks blocks of n_tokens tokens in one launch (the queued
+ * blocks of one step): x [n_blocks][n_tokens][dim], q [n_blocks][n_tokens]
+ * [heads][head_dim] or NULL, block b's K/V into ring slot slots[b] (host
+ * array; 1 <= n_blocks <= 64, slots distinct).  rope: NULL, or block b's
+ * pair-major table at rope + b * rope_block_stride floats (stride 0: one
+ * table for every block, else >= n_tokens * head_dim).  Each block's outputs
+ * are bit-identical to a ba_qkv_project call on that block alone. */
+ba_status ba_qkv_project_batched(const void* x, int32_t n_blocks, int32_t n_tokens, int32_t dim, const void* w,
+                                 void* q, const ba_ring* cache, const int32_t* slots, const float* rope,
+                                 int64_t rope_block_stride, hipStream_t stream);
+
 /*
  * Noise schedule of the per-block update.  NULL selects the default
  * {T = 1000, stride = 20, beta_start = 1e-4, beta_end = 0.02, BA_SCHED_DDIM}.

@@ -21,7 +21,7 @@ FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dere
 
 def test_exports_every_declared_symbol():
     names = B.header_symbols()
-    assert len(names) == 19
+    assert len(names) == 20
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -277,6 +277,18 @@ def test_project_rejects():
     assert f(FAKE, 100, 0, FAKE, FAKE, rr, 1, None, None) == B.BA_ERR_OUT_OF_RANGE
     r32 = _ring(n_slots=2, slot_tokens=100, heads=2, head_dim=64, dtype=B.BA_F32)
     assert f(FAKE, 100, 128, FAKE, FAKE, ctypes.byref(r32), 1, None, None) == B.BA_ERR_UNSUPPORTED
+    g = B.raw.ba_qkv_project_batched
+    r4 = ctypes.byref(_ring(n_slots=4, slot_tokens=100, heads=2, head_dim=64))
+    sl = (ctypes.c_int32 * 3)(0, 2, 3)
+    assert g(FAKE, 0, 100, 128, FAKE, FAKE, r4, sl, None, 0, None) == B.BA_ERR_OUT_OF_RANGE      # n_blocks
+    assert g(FAKE, 65, 100, 128, FAKE, FAKE, r4, sl, None, 0, None) == B.BA_ERR_OUT_OF_RANGE
+    assert g(FAKE, 3, 100, 128, FAKE, FAKE, r4, None, None, 0, None) == B.BA_ERR_INVALID_ARG     # slots NULL
+    dup = (ctypes.c_int32 * 3)(0, 2, 0)
+    assert g(FAKE, 3, 100, 128, FAKE, FAKE, r4, dup, None, 0, None) == B.BA_ERR_INVALID_ARG      # shared slot
+    bad = (ctypes.c_int32 * 3)(0, 2, 4)
+    assert g(FAKE, 3, 100, 128, FAKE, FAKE, r4, bad, None, 0, None) == B.BA_ERR_OUT_OF_RANGE
+    assert g(FAKE, 3, 100, 128, FAKE, FAKE, r4, sl, FAKE, 100, None) == B.BA_ERR_INVALID_ARG     # table stride
+    assert "rope_block_stride" in B.ba_last_error()
 
 
 @pytest.mark.parametrize("pool,excl,bf", [(21, 3, 4), (21, 0, 21), (9, 8, 1), (64, 0, 64), (200, 17, 64), (5, 1, 3)])

@@ -117,3 +117,49 @@ def test_producer_feeds_attention_like_append():
     B.ba_cache_append_batched(r2, to_dev(k[None], "bf16"), to_dev(v[None], "bf16"), [1])
     torch.cuda.synchronize()
     assert ring_bytes(r1) == ring_bytes(r2)
+
+
+@pytest.mark.parametrize("per_block_rope", [False, True])
+def test_batched_producer_equals_single_calls(per_block_rope):
+    # one launch over three blocks writes, bit for bit, what three single
+    # calls write; and meets the bar against the oracle block by block
+    import torch
+    import block_wise_long_amd as B
+    rng = np.random.Generator(np.random.PCG64(31 + per_block_rope))
+    nb, L, dim, H, D = 3, 230, 192, 1, 64
+    x = draw(rng, (nb, L, dim), 1.0, "bf16")
+    w = draw(rng, (3 * H * D, dim), dim ** -0.5, "bf16")
+    tabs = []
+    for _ in range(nb if per_block_rope else 1):
+        ang = rng.uniform(-40.0, 40.0, (L, D // 2))
+        tabs.append(np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32))
+    dev_tab = torch.from_numpy(np.stack([t.transpose(1, 0, 2) for t in tabs]).copy()).cuda()
+    slots = [4, 0, 2]
+    r1 = B.ba_ring_init(5, L + 10, H, D, B.BA_BF16)
+    r2 = B.ba_ring_init(5, L + 10, H, D, B.BA_BF16)
+    q1 = torch.full((nb, L, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    q2 = torch.full((nb, L, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xd, wd = to_dev(x, "bf16"), to_dev(w, "bf16")
+    B.ba_qkv_project_batched(xd, wd, r1, slots, q=q1, rope=dev_tab if per_block_rope else dev_tab[0])
+    for b in range(nb):
+        B.ba_qkv_project(xd[b], wd, r2, slots[b], q=q2[b], rope=dev_tab[b if per_block_rope else 0])
+    torch.cuda.synchronize()
+    assert ring_bytes(r1) == ring_bytes(r2)
+    assert np.array_equal(to_host_bits(q1), to_host_bits(q2))
+    model = oring.RingModel(5, L + 10, H, D, "bf16")
+    buf = np.frombuffer(ring_bytes(r1), dtype=np.uint16)
+    absw = np.abs(N.bf16_bits_to_f64(w))
+    for b in range(nb):
+        tab = tabs[b if per_block_rope else 0]
+        qe, ke, ve = P.qkv_project_ref(x[b], w, H, D, tab)
+        bound = (2.0 ** -21) * (np.abs(N.bf16_bits_to_f64(x[b])) @ absw.T)
+        bq, bk, bv = (bound[:, j * H * D:(j + 1) * H * D].reshape(L, H, D) for j in range(3))
+        pr = lambda t: t + t.reshape(L, H, D // 2, 2)[..., ::-1].reshape(L, H, D)
+        _check(to_host_bits(q1)[b], qe, pr(bq))
+        got_k = np.stack([buf[[model.k_offset(slots[b], 0, t, d) for d in range(D)]] for t in range(L)])[:, None]
+        got_v = np.stack([buf[[model.v_offset(slots[b], 0, t, d) for d in range(D)]] for t in range(L)])[:, None]
+        _check(got_k, ke, pr(bk))
+        _check(got_v, ve, bv)
+    # the ring's untouched slots stay zero
+    for s in (1, 3):
+        assert not any(buf[model.k_offset(s, 0, t, 0)] for t in range(L))

@@ -108,3 +108,62 @@ def test_queue_pops_in_order_and_every_block_reaches_zero():
     for k, ts in seen_t.items():
         if k >= n and len(ts) == n:
             assert ts == [T - j * s for j in range(n)]
+
+
+def _within_ulp(got, exact, bound):
+    mag = np.abs(exact) + bound
+    ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(mag, 2.0 ** -126))).astype(int) - 7)
+    return not (np.abs(got - exact) > ulp + bound).any()
+
+
+def test_queue_with_projection_layer():
+    # the queue's layer through the fused K/V producer: each block's latents
+    # ([tokens][dim]) projected to q (buffer) and K/V (its ring slot, no
+    # append); checked per step against the oracle's projection of the same
+    # latents, then attention from the GPU's own q and ring
+    import torch
+    from block_wise_long_amd.fifo import FifoQueue
+    from oracle import projection as P
+
+    rng = np.random.Generator(np.random.PCG64(404))
+    n, L, H, D, TXT, T = 3, 100, 2, 64, 16, 30
+    dim = H * D
+    x0 = draw(rng, (n, L, H, D), 0.5, "bf16")
+    w = draw(rng, (3 * H * D, dim), dim ** -0.5, "bf16")
+    ang = rng.uniform(-20.0, 20.0, (L, D // 2))
+    table = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)     # [L][D/2][2]
+    tk = draw(rng, (TXT, H, D), 0.5, "bf16")
+    tv = draw(rng, (TXT, H, D), 0.5, "bf16")
+    layer = {"w": to_dev(w, "bf16"), "rope": torch.from_numpy(table.transpose(1, 0, 2).copy()).cuda()}
+    fq = FifoQueue(to_dev(x0, "bf16"), to_dev(tk, "bf16"), to_dev(tv, "bf16"), T=T, layer=layer)
+    otext = oring.RingModel(1, TXT, H, D, "bf16")
+    otext.append(tk, tv, TXT)
+    absw = np.abs(N.bf16_bits_to_f64(w))
+
+    def partner(b):     # a rotated pair mixes both members' errors
+        return b + b.reshape(L, H, D // 2, 2)[..., ::-1].reshape(L, H, D)
+    for g in range(2 * n + 2):
+        pre = to_host_bits(fq.x)
+        fq.step(to_dev(draw(rng, (L, H, D), 0.5, "bf16"), "bf16"))
+        torch.cuda.synchronize()
+        slots, _, ts, stride = fq.last_plan
+        plan, ostride = OQ.plan(n, T, L, TXT, g, g)
+        assert slots == [e["write_slot"] for e in plan] and ts == [e["t"] for e in plan]
+        model = oring.RingModel(2 * n, L, H, D, "bf16")
+        model.mem[:] = np.frombuffer(ring_bytes(fq.ring), dtype=model.mem.dtype)
+        qg = N.bf16_bits_to_f64(to_host_bits(fq.qbuf))
+        for m in range(n):
+            xm = pre[m].reshape(L, dim)
+            qe, ke, ve = P.qkv_project_ref(xm, w, H, D, table)
+            bound = (2.0 ** -21) * (np.abs(N.bf16_bits_to_f64(xm)) @ absw.T)
+            bq, bk, bv = (bound[:, j * dim:(j + 1) * dim].reshape(L, H, D) for j in range(3))
+            gk = np.stack([model.keys(slots[m], h, L) for h in range(H)], axis=1)
+            gv = np.stack([model.values(slots[m], h, L) for h in range(H)], axis=1)
+            assert _within_ulp(qg[m], qe, partner(bq)), (g, m, "q")
+            assert _within_ulp(gk, ke, partner(bk)), (g, m, "k")
+            assert _within_ulp(gv, ve, bv), (g, m, "v")
+        # attention over each block's key set from the GPU's own q and ring
+        ref, _ = A.block_attention_ref(qg, model, otext, [e["meta"] for e in plan])
+        got = decode(to_host_bits(fq.pred), "bf16")
+        check_contract(got, ref, "bf16", gate2=False)
+        assert np.abs(got - ref).max() <= 4 * 2.0 ** -8 * np.abs(ref).max()
