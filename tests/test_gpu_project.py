@@ -163,3 +163,48 @@ def test_batched_producer_equals_single_calls(per_block_rope):
     # the ring's untouched slots stay zero
     for s in (1, 3):
         assert not any(buf[model.k_offset(s, 0, t, 0)] for t in range(L))
+
+
+def test_producer_at_480p_shape_sampled():
+    # the bench's launch: 5400 tokens x 1536 -> 4608 rows (24 heads x 64),
+    # rotation on, one block and the 8-block batch; sampled tokens (tile
+    # edges, the ragged tail, random) checked in every output row
+    import torch
+    import block_wise_long_amd as B
+    rng = np.random.Generator(np.random.PCG64(480))
+    nb, L, H, D = 8, 5400, 24, 64
+    dim = H * D
+    x = draw(rng, (nb, L, dim), 1.0, "bf16")
+    w = draw(rng, (3 * H * D, dim), dim ** -0.5, "bf16")
+    pos = np.arange(L, dtype=np.float64)[:, None]
+    freq = 10000.0 ** (-np.arange(D // 2, dtype=np.float64) * 2 / D)[None, :]
+    ang = pos * freq
+    table = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)      # [L][D/2][2]
+    tdev = torch.from_numpy(table.transpose(1, 0, 2).copy()).cuda()
+    ring = B.ba_ring_init(nb + 1, L, H, D, B.BA_BF16)
+    q1 = torch.empty((L, H, D), dtype=torch.bfloat16, device="cuda")
+    qb = torch.empty((nb, L, H, D), dtype=torch.bfloat16, device="cuda")
+    xd, wd = to_dev(x, "bf16"), to_dev(w, "bf16")
+    B.ba_qkv_project(xd[0], wd, ring, nb, q=q1, rope=tdev)                 # one block into the last slot
+    B.ba_qkv_project_batched(xd, wd, ring, list(range(nb)), q=qb, rope=tdev)
+    torch.cuda.synchronize()
+    toks = sorted({0, 1, 255, 256, 511, 512, 5119, 5120, 5375, 5376, 5398, 5399}
+                  | set(rng.integers(0, L, 20).tolist()))
+    model = oring.RingModel(nb + 1, L, H, D, "bf16")
+    buf = np.frombuffer(ring_bytes(ring), dtype=np.uint16)
+    absw = np.abs(N.bf16_bits_to_f64(w))
+    hh, tt, dd = np.meshgrid(np.arange(H), np.array(toks), np.arange(D), indexing="ij")
+    for b, slot, qt in [(0, nb, q1), (0, 0, qb[0]), (5, 5, qb[5]), (7, 7, qb[7])]:
+        xs = x[b][toks]
+        qe, ke, ve = P.qkv_project_ref(xs, w, H, D, table[toks])
+        bound = (2.0 ** -21) * (np.abs(N.bf16_bits_to_f64(xs)) @ absw.T)
+        n = len(toks)
+        bq, bk, bv = (bound[:, j * dim:(j + 1) * dim].reshape(n, H, D) for j in range(3))
+        pr = lambda t: t + t.reshape(n, H, D // 2, 2)[..., ::-1].reshape(n, H, D)
+        _check(to_host_bits(qt)[toks], qe, pr(bq))
+        got_k = buf[model.k_offset(slot, hh, tt, dd)].transpose(1, 0, 2)         # [n][H][D]
+        got_v = buf[model.v_offset(slot, hh, tt, dd)].transpose(1, 0, 2)
+        _check(got_k, ke, pr(bk))
+        _check(got_v, ve, bv)
+    # the one-block call and block 0 of the batch agree bit for bit
+    assert np.array_equal(to_host_bits(q1), to_host_bits(qb[0]))
