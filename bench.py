@@ -92,9 +92,15 @@ def cpu_baseline(cfg, inputs, budget_s):
             break
     dt = time.perf_counter() - t0
     flops = 4.0 * cfg.q_len * cfg.key_len * cfg.head_dim * heads
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:  # noqa: BLE001
+        affinity = None
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} of {cfg.heads} heads, all {cfg.q_len} queries over all {cfg.key_len} keys, "
-                      f"fp64 numpy (BLAS dgemm), {dt:.1f} s wall"}
+                      f"fp64 numpy (BLAS dgemm), {dt:.1f} s wall",
+            "gflops_fp64": round(flops / dt / 1e9, 2), "os_cpu_count": os.cpu_count(),
+            "sched_affinity": affinity, "blas_threads": threads}
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
@@ -565,6 +571,7 @@ def main():
     }
     if args.cpu_budget > 0 and cfg.n_blocks == 1 and not cfg.full_sequence:
         res["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_budget)
+        res["cpu_baseline"]["gpu_over_oracle"] = round(tflops_attn / res["cpu_baseline"]["value"], 1)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
