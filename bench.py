@@ -420,30 +420,30 @@ def main():
         return
     if args.noise:
         if args.gpus != 1:
-            print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+            print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1"}))
             sys.exit(2)
         noise_bench(args)
         return
     if args.cross:
         if args.gpus != 1:
-            print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+            print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1"}))
             sys.exit(2)
         cross_bench(args)
         return
     if args.project:
         if args.gpus != 1:
-            print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+            print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1"}))
             sys.exit(2)
         project_bench(args)
         return
     if args.queue:
         if args.gpus != 1:
-            print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+            print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1"}))
             sys.exit(2)
         queue_bench(args)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
