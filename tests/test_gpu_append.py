@@ -58,3 +58,16 @@ def test_rejected_append_leaves_ring_alone():
     with pytest.raises(B.BlockAttnError):
         B.ba_cache_append_batched(w.ring, to_dev(k, "bf16"), to_dev(k, "bf16"), [1, 1])
     assert ring_bytes(w.ring) == w.oring.as_bytes()
+
+
+def test_batched_append_more_slots_than_one_launch_takes():
+    # 70 blocks: launches of 64 and 6 slots, bit-exact against the ring model
+    rng = _rng(70)
+    H, D, n, nb = 1, 64, 40, 70
+    w = Workload("bf16", 80, n, H, D, 0)
+    slots = [(7 * b + 3) % 80 for b in range(nb)]          # distinct, scattered
+    assert len(set(slots)) == nb
+    k = draw(rng, (nb, n, H, D), 0.5, "bf16")
+    v = draw(rng, (nb, n, H, D), 0.5, "bf16")
+    w.append_batched(k, v, slots)
+    assert ring_bytes(w.ring) == w.oring.as_bytes()

@@ -237,3 +237,27 @@ def test_in_place_output():
     B.ba_block_attention(qd, w.ring, None, metas, out=qd)
     torch.cuda.synchronize()
     assert torch.equal(qd.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("workspace", ["auto", None])
+def test_more_blocks_than_one_launch_takes(workspace):
+    # 21 blocks: the call runs as launches of 16 and 5 blocks, each with its
+    # own q / out / lse offsets; every block checked against the oracle
+    rng = _rng(21)
+    H, D, L, nb = 2, 64, 96, 21
+    w = Workload("bf16", 5, L, H, D, 24)
+    _fill(w, rng, (L, 90, L, 40, L), H, D, "bf16", 0.5, 24)
+    q = draw(rng, (nb, 100, H, D), 0.5, "bf16")
+    metas = []
+    for b in range(nb):
+        segs = [((b + i) % 5, (L, 90, L, 40, L)[(b + i) % 5]) for i in range(1 + b % 3)]
+        metas.append({"q_len": 100 - (b % 4) * 13, "segs": segs, "text_slot": 0, "text_len": (b * 5) % 25})
+    out, lse = w.run(q, metas, workspace=workspace)
+    ref, ref_lse = w.oracle(q, metas)
+    got = decode(out, "bf16")
+    check_contract(got, ref, "bf16", gate2=False)
+    rms = math.sqrt(np.nanmean(ref ** 2))
+    assert np.nanmax(np.abs(got - ref)) <= 2 ** -7 * np.nanmax(np.abs(ref)) + 0.05 * rms
+    assert np.nanmax(np.abs(lse.cpu().numpy() - ref_lse)) < 2e-3
+    for b in range(nb):        # rows past each q_len untouched
+        assert np.isnan(got[b, metas[b]["q_len"]:]).all()
