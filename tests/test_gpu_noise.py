@@ -65,3 +65,17 @@ def test_queue_draws_new_blocks_from_the_pool():
         ref = NZ.noise_block_ref(pool, C, F, frames)
         got = to_host_bits(fq.x)[head].reshape(C, 3, E)
         assert np.array_equal(got, ref), g
+
+
+def test_gather_at_the_grid_limit():
+    # channels x block_frames = 64 x 64 = 4096 grid rows, frames of one vector
+    import torch
+    import block_wise_long_amd as B
+    rng = _rng(4096)
+    C, F, E, bf = 64, 70, 8, 64
+    pool = draw(rng, (C, F, E), 1.0, "bf16")
+    frames = B.ba_noise_assign(9, 3, F, 6, bf)
+    out = torch.empty((C, bf, E), dtype=torch.bfloat16, device="cuda")
+    B.ba_noise_block(to_dev(pool, "bf16"), frames, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(out), NZ.noise_block_ref(pool, C, F, frames))

@@ -208,3 +208,23 @@ def test_producer_at_480p_shape_sampled():
         _check(got_v, ve, bv)
     # the one-block call and block 0 of the batch agree bit for bit
     assert np.array_equal(to_host_bits(q1), to_host_bits(qb[0]))
+
+
+def test_batched_producer_at_the_block_limit():
+    # 64 blocks (the largest batch) of a small shape: every slot written as
+    # by its own single call, bit for bit
+    import torch
+    import block_wise_long_amd as B
+    rng = np.random.Generator(np.random.PCG64(64))
+    nb, L, dim, H, D = 64, 70, 64, 1, 64
+    x = to_dev(draw(rng, (nb, L, dim), 1.0, "bf16"), "bf16")
+    w = to_dev(draw(rng, (3 * H * D, dim), dim ** -0.5, "bf16"), "bf16")
+    slots = [(5 * b + 1) % nb for b in range(nb)]
+    r1 = B.ba_ring_init(nb, L, H, D, B.BA_BF16)
+    r2 = B.ba_ring_init(nb, L, H, D, B.BA_BF16)
+    B.ba_qkv_project_batched(x, w, r1, slots)
+    for b in range(nb):
+        B.ba_qkv_project(x[b], w, r2, slots[b])
+    torch.cuda.synchronize()
+    assert ring_bytes(r1) == ring_bytes(r2)
+    assert any(ring_bytes(r1))
