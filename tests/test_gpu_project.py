@@ -228,3 +228,35 @@ def test_batched_producer_at_the_block_limit():
     torch.cuda.synchronize()
     assert ring_bytes(r1) == ring_bytes(r2)
     assert any(ring_bytes(r1))
+
+
+def test_producer_at_720p_shape_sampled():
+    # 7800 tokens x 5120 -> 15360 rows (40 heads x 128), rotation on, q
+    # skipped (only the k and v rows computed); sampled tokens in every row
+    import torch
+    import block_wise_long_amd as B
+    rng = np.random.Generator(np.random.PCG64(720))
+    L, H, D = 7800, 40, 128
+    dim = H * D
+    x = draw(rng, (L, dim), 1.0, "bf16")
+    w = draw(rng, (3 * H * D, dim), dim ** -0.5, "bf16")
+    ang = rng.uniform(-60.0, 60.0, (L, D // 2))
+    table = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    ring = B.ba_ring_init(2, L, H, D, B.BA_BF16)
+    B.ba_qkv_project(to_dev(x, "bf16"), to_dev(w, "bf16"), ring, 1,
+                     rope=torch.from_numpy(table.transpose(1, 0, 2).copy()).cuda())
+    torch.cuda.synchronize()
+    toks = sorted({0, 255, 256, 7679, 7680, 7798, 7799} | set(rng.integers(0, L, 12).tolist()))
+    n = len(toks)
+    _, ke, ve = P.qkv_project_ref(x[toks], w, H, D, table[toks])
+    bound = (2.0 ** -21) * (np.abs(N.bf16_bits_to_f64(x[toks])) @ np.abs(N.bf16_bits_to_f64(w)).T)
+    bk, bv = (bound[:, j * dim:(j + 1) * dim].reshape(n, H, D) for j in (1, 2))
+    model = oring.RingModel(2, L, H, D, "bf16")
+    buf = np.frombuffer(ring_bytes(ring), dtype=np.uint16)
+    hh, tt, dd = np.meshgrid(np.arange(H), np.array(toks), np.arange(D), indexing="ij")
+    pr = lambda t: t + t.reshape(n, H, D // 2, 2)[..., ::-1].reshape(n, H, D)
+    _check(buf[model.k_offset(1, hh, tt, dd)].transpose(1, 0, 2), ke, pr(bk))
+    _check(buf[model.v_offset(1, hh, tt, dd)].transpose(1, 0, 2), ve, bv)
+    # the slot's padded tail (7800 .. 7807) reads as zeros, slot 0 untouched
+    tail = buf[model.k_offset(1, hh[:, :1], np.full_like(tt[:, :1], L), dd[:, :1])]
+    assert not tail.any() and not buf[model.k_offset(0, hh, tt, dd)].any()
