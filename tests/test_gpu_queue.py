@@ -167,3 +167,54 @@ def test_queue_with_projection_layer():
         got = decode(to_host_bits(fq.pred), "bf16")
         check_contract(got, ref, "bf16", gate2=False)
         assert np.abs(got - ref).max() <= 4 * 2.0 ** -8 * np.abs(ref).max()
+
+
+def test_queue_at_bench_shape_sampled():
+    # the bench's queue: 8 blocks of 5400 tokens x 24 heads x 64, 226 text
+    # keys, T = 1000; two steps (the second with neighbour context): plan,
+    # this step's ring slots, sampled rows of the attention against the oracle
+    # on the GPU's own ring and latents, the update on sampled elements
+    import torch
+    from block_wise_long_amd.fifo import FifoQueue
+    from _util import sample_rows
+
+    rng = np.random.Generator(np.random.PCG64(2054))
+    n, L, H, D, TXT, T = 8, 5400, 24, 64, 226, 1000
+    x0 = draw(rng, (n, L, H, D), 0.5, "bf16")
+    tk = draw(rng, (TXT, H, D), 0.5, "bf16")
+    tv = draw(rng, (TXT, H, D), 0.5, "bf16")
+    fq = FifoQueue(to_dev(x0, "bf16"), to_dev(tk, "bf16"), to_dev(tv, "bf16"), T=T)
+    otext = oring.RingModel(1, TXT, H, D, "bf16")
+    otext.append(tk, tv, TXT)
+    rows = sample_rows(L, 8, seed=54)
+    heads = [0, 11, 23]
+    for g in range(2):
+        pre = to_host_bits(fq.x)
+        head = fq.head_slot
+        done = fq.step(to_dev(draw(rng, (L, H, D), 0.5, "bf16"), "bf16"))
+        torch.cuda.synchronize()
+        slots, _, ts, stride = fq.last_plan
+        plan, _ = OQ.plan(n, T, L, TXT, g, g)
+        assert slots == [e["write_slot"] for e in plan] and ts == [e["t"] for e in plan] and stride == 125
+        model = oring.RingModel(2 * n, L, H, D, "bf16")
+        model.mem[:] = np.frombuffer(ring_bytes(fq.ring), dtype=model.mem.dtype)
+        for m in range(n):          # this step's appends: each block's latents in its write slot
+            for h in heads:
+                assert np.array_equal(model.keys(slots[m], h, L)[rows], N.bf16_bits_to_f64(pre[m, rows, h]))
+                assert np.array_equal(model.values(slots[m], h, L)[rows], N.bf16_bits_to_f64(pre[m, rows, h]))
+        ref, _ = A.block_attention_ref(N.bf16_bits_to_f64(pre), model, otext, [e["meta"] for e in plan],
+                                       heads=heads, rows=rows)
+        pred = to_host_bits(fq.pred)
+        # after one update the stand-in latents are no longer N(0, 0.25) (the
+        # attention output is not the noise), scores grow and |o| reaches ~6:
+        # the contract plus 4 bf16 ulps of the largest output, as above
+        got = decode(pred, "bf16")
+        check_contract(got, ref, "bf16", gate2=False)
+        assert np.nanmax(np.abs(got - ref)) <= 4 * 2.0 ** -8 * np.nanmax(np.abs(ref))
+        # the update from the same inputs; the head's updated block left the queue
+        post = to_host_bits(fq.x)
+        post[head] = to_host_bits(done)
+        idx = rng.integers(0, L * H * D, 4096)
+        xs, es = pre.reshape(n, -1)[:, idx], pred.reshape(n, -1)[:, idx]
+        upd = S.block_update_ref(xs, es, ts, T=T, stride=stride)
+        _bf16_close(post.reshape(n, -1)[:, idx], upd, xs, es, ts, T, stride, "ddim", 1.0)
