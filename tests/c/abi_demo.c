@@ -10,6 +10,9 @@
  * file:  int32 header {magic, L, H, D, TXT, E, t} then uint16 arrays q, k_ctx,
  *        v_ctx, k_cur, v_cur, k_txt, v_txt ([tokens][H][D] each), out
  *        ([L][H][D]), x, eps, x_after ([E] each); all bf16 bit patterns.
+ *        Then the host bookkeeping, int32: the noise assignment of block 3
+ *        (seed 7, pool 21, 3 excluded, 4 frames) and, for a 4-block queue
+ *        (T 1000) at its third step, every block's write slot and timestep.
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -138,6 +141,22 @@ int main(int argc, char** argv) {
   const uint16_t* arrays[] = {q, kc, vc, ku, vu, kt, vt, out, x, eps, xa};
   const size_t counts[] = {blk, blk, blk, blk, blk, tblk, tblk, blk, (size_t)E, (size_t)E, (size_t)E};
   for (int i = 0; i < 11; ++i) fwrite(arrays[i], 2, counts[i], f);
+
+  /* host bookkeeping through the same ABI: a block's noise frames, a queue plan */
+  int32_t frames[4];
+  CHECK_BA(ba_noise_assign(7, 3, 21, 3, 4, frames));
+  fwrite(frames, 4, 4, f);
+  ba_queue q4;
+  CHECK_BA(ba_queue_init(&q4, 4, 1000, L, TXT));
+  int32_t wslots[4], tq[4], stride = 0;
+  ba_block_meta qm[4];
+  for (int g = 0; g < 2; ++g) {
+    CHECK_BA(ba_queue_plan(&q4, wslots, qm, tq, &stride));
+    CHECK_BA(ba_queue_advance(&q4));
+  }
+  CHECK_BA(ba_queue_plan(&q4, wslots, qm, tq, &stride));
+  fwrite(wslots, 4, 4, f);
+  fwrite(tq, 4, 4, f);
   fclose(f);
   printf("abi_demo ok: slots ctx %d cur %d text %d, library %d\n", slot_ctx, slot_cur, slot_txt, ba_version());
   return 0;

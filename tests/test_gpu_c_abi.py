@@ -31,13 +31,21 @@ def test_plain_c_caller(tmp_path):
     hdr = np.frombuffer(raw[:28], dtype=np.int32)
     magic, L, H, D, TXT, E, t = (int(v) for v in hdr)
     assert magic == 0x62616331
-    data = np.frombuffer(raw[28:], dtype=np.uint16)
     sizes = [L * H * D] * 5 + [TXT * H * D] * 2 + [L * H * D] + [E] * 3
+    data = np.frombuffer(raw[28:28 + 2 * sum(sizes)], dtype=np.uint16)
     parts, off = [], 0
     for n in sizes:
         parts.append(data[off:off + n])
         off += n
-    assert off == data.size
+    tail = np.frombuffer(raw[28 + 2 * sum(sizes):], dtype=np.int32)
+    assert tail.size == 12
+    # host bookkeeping from C: the noise frames and the queue plan at step 2
+    from oracle import noise as NZ
+    from oracle import queue as OQ
+    assert tail[:4].tolist() == NZ.assign(7, 3, 21, 3, 4)
+    plan, _ = OQ.plan(4, 1000, L, TXT, 2, 2)
+    assert tail[4:8].tolist() == [e["write_slot"] for e in plan]
+    assert tail[8:12].tolist() == [e["t"] for e in plan]
     q, kc, vc, ku, vu, kt, vt, out, x, eps, xa = parts
     blk = lambda a, n: a.reshape(n, H, D)
     ring = oring.RingModel(2, L, H, D, "bf16")
