@@ -151,7 +151,7 @@ const char* ba_status_string(ba_status s) {
 
 const char* ba_last_error(void) { return g_err; }
 
-int32_t ba_version(void) { return 1 * 10000 + 2 * 100 + 0; }
+int32_t ba_version(void) { return 1 * 10000 + 3 * 100 + 0; }
 
 size_t ba_ring_bytes(int32_t n_slots, int32_t slot_tokens, int32_t heads, int32_t head_dim,
                      int32_t dtype) {
@@ -236,6 +236,12 @@ ba_status ba_cache_append_batched(const ba_ring* ring, const void* k, const void
     return st != BA_OK ? st : ok();
   }
   return append_common(ring, k, v, n_tokens, slots, n_blocks, stream);
+}
+
+int32_t ba_attention_query_tile(int32_t head_dim, int32_t dtype) {
+  if (dtype == BA_BF16 && (head_dim == 64 || head_dim == 128)) return ba::attention_bf16_q_tile(head_dim);
+  if (dtype == BA_F32 && (head_dim == 64 || head_dim == 128)) return ba::attention_f32_q_tile();
+  return 0;
 }
 
 size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_blocks, int32_t q_stride,

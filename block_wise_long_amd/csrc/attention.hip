@@ -121,7 +121,10 @@ struct WaveState {
 // 4 waves, three workgroups per CU; D = 128: 8 waves sharing one set of LDS
 // buffers, one workgroup per CU.
 template <int D> struct Shape;
-template <> struct Shape<64> { static constexpr int NW = 4, WAVES_PER_SIMD = 3; };
+#ifndef BA_NW64
+#define BA_NW64 12
+#endif
+template <> struct Shape<64> { static constexpr int NW = BA_NW64, WAVES_PER_SIMD = 3; };
 template <> struct Shape<128> { static constexpr int NW = 8, WAVES_PER_SIMD = 2; };
 
 constexpr int kBuffers = 3;   // LDS tile buffers: in use, being consumed, being filled
@@ -141,9 +144,8 @@ struct Tile {
   static constexpr int K_CH = kKTile * KCH;          // chunks of the K tile
   static constexpr int V_CH = D * (kKTile / 8);      // chunks of the V^T tile
   static constexpr int CH = K_CH + V_CH;
-  static constexpr int K_LOADS = K_CH / THREADS;
-  static constexpr int LOADS = CH / THREADS;
-  static_assert(K_CH % THREADS == 0 && V_CH % THREADS == 0, "tile shape");
+  static constexpr int LOADS = (CH + THREADS - 1) / THREADS;   // copy rounds per tile
+  static_assert(K_CH % 64 == 0 && CH % 64 == 0, "a wave's chunks are all K or all V");
 
   // XOR swizzle of the 16-byte chunks of a row.  A b128 LDS access is served
   // 8 lanes per 128 bytes or 16 lanes per 256 bytes of banks; consecutive
@@ -168,14 +170,15 @@ __device__ __forceinline__ void load_tile(const Cursor& c, int tid, unsigned buf
   const uint16_t* kb = c.k + (int64_t)c.off * D;   // uniform tile bases
   const uint16_t* vb = c.v + c.off;
   const int lane = tid & 63;
-  const int wave_base = tid & ~63;
+  const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);   // uniform
 #pragma unroll
   for (int u = 0; u < T::LOADS; ++u) {
     const int p0 = u * T::THREADS + wave_base;     // first LDS chunk of this wave
+    if (T::CH % T::THREADS != 0 && p0 >= T::CH) break;   // last round: fewer waves
     const int p = p0 + lane;
     const uint16_t* base;                          // uniform
     unsigned idx;                                  // per lane, in elements
-    if (u < T::K_LOADS) {
+    if (p0 < T::K_CH) {
       const int r = p / T::KCH, pos = p % T::KCH;
       const int ch = D == 64 ? (pos ^ T::row_swz128(r)) : (pos ^ (r & 15));
       base = kb;
@@ -193,7 +196,7 @@ __device__ __forceinline__ void load_tile(const Cursor& c, int tid, unsigned buf
     // buffer.  Seen by the compiler as an LDS write in flight, it would make
     // every LDS read of the steps wait for all outstanding LDS reads.
     const unsigned lds_base = buf_lds + 16u * (unsigned)(u * T::THREADS) +
-                              16u * (unsigned)__builtin_amdgcn_readfirstlane(wave_base);
+                              16u * (unsigned)wave_base;
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(idx * 2u), "s"(base), "s"(lds_base)
@@ -578,7 +581,8 @@ void attention_bf16_kernel(const AttnArgs a) {
       // buffer 2 starts as zeros: the first step's deferred PV reads it
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int u = 0; u < T::LOADS; ++u) lds[2][u * T::THREADS + tid] = z;
+      for (int u = 0; u < T::LOADS; ++u)
+        if (T::CH % T::THREADS == 0 || u * T::THREADS + tid < T::CH) lds[2][u * T::THREADS + tid] = z;
     }
     WaveState<D> w;
 #pragma unroll

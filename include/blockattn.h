@@ -176,6 +176,11 @@ ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cac
 size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_blocks,
                                     int32_t q_stride, int32_t heads);
 
+/* Queries of one head that one workgroup of ba_block_attention takes (its
+ * query tile): a block of q_len queries is heads * ceil(q_len / tile) tasks.
+ * 0 for a head_dim / dtype pair the call does not support.  Needs no device. */
+int32_t ba_attention_query_tile(int32_t head_dim, int32_t dtype);
+
 /* The schedule ba_block_attention would take for these arguments and a
  * workspace of workspace_bytes (0: none), without launching anything:
  * *tail_workgroups = tail workgroups per XCD sharing the split (the largest

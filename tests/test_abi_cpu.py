@@ -21,11 +21,11 @@ FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dere
 
 def test_exports_every_declared_symbol():
     names = B.header_symbols()
-    assert len(names) == 20
+    assert len(names) == 21
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert B.ba_version() == 10200
+    assert B.ba_version() == 10300
 
 
 @pytest.mark.parametrize("shape", [(2, 5400, 24, 64), (16, 5400, 24, 64), (2, 7800, 40, 128), (1, 226, 24, 64),
@@ -198,6 +198,11 @@ def test_attention_plan_on_the_host():
 
 def test_workspace_bytes_without_device():
     # fp32 never uses one; with no device to size the grid, none is asked for
+    # query tiles: whole waves of 32 queries (bf16), 64 (fp32); 0 when unsupported
+    for d in (64, 128):
+        assert B.ba_attention_query_tile(d, B.BA_BF16) % 32 == 0 and B.ba_attention_query_tile(d, B.BA_BF16) >= 128
+        assert B.ba_attention_query_tile(d, B.BA_F32) == 64
+    assert B.ba_attention_query_tile(96, B.BA_BF16) == 0 and B.ba_attention_query_tile(64, 7) == 0
     assert B.ba_attention_workspace_bytes(64, B.BA_F32, 1, 128, 2) == 0
     assert B.ba_attention_workspace_bytes(96, B.BA_BF16, 1, 128, 2) == 0
     assert B.ba_attention_workspace_bytes(64, B.BA_BF16, 0, 128, 2) == 0

@@ -17,10 +17,11 @@ def _rng(s):
 
 
 def _setup(D, seed):
-    # long enough key sets (25-52 tiles of 64 per task) that the library
-    # takes the split schedule with 1, 2 and 5 tail workgroups per XCD
+    # long enough key sets (25-52 tiles of 64 per task) and enough tasks
+    # (12 heads: 48-84 query tiles) that the library takes the split schedule
+    # with 1, 2 and 5 tail workgroups per XCD
     rng = _rng(seed)
-    H = 6
+    H = 12
     w = Workload("bf16", 6, 1600, H, D, 120)
     for n in (1600, 1500, 1600, 33, 1600, 1599):
         w.append(draw(rng, (n, H, D), 0.5, "bf16"), draw(rng, (n, H, D), 0.5, "bf16"))
@@ -37,7 +38,10 @@ def _workspace(D, tail_wg, fill):
     """A workspace with room for exactly tail_wg tail workgroups per XCD,
     pre-filled with garbage (its contents must not matter)."""
     import torch
-    part = {64: 4 * 4 * (2 * 16 * 64 + 2 * 64), 128: 4 * 8 * (4 * 16 * 64 + 2 * 64)}[D]
+    import block_wise_long_amd as B
+    # one partial result per query of the query tile: head_dim fp32 output
+    # values, and the fp32 maximum and sum of each of its two lanes
+    part = 4 * B.ba_attention_query_tile(D, B.BA_BF16) * (D + 4)
     nbytes = 16 * tail_wg * part
     ws = torch.full((nbytes + 256,), fill, dtype=torch.uint8, device="cuda")
     off = (-ws.data_ptr()) % 256
