@@ -9,7 +9,9 @@
 // and the text-conditioning K/V.
 //
 // bf16 kernel (gfx950, v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//   * workgroup = 4 waves = 128 queries of one (block, head); wave = 32 queries.
+//   * workgroup = one query tile of one (block, head): 12 waves (384 queries)
+//     at head dim 64, 8 waves (256) at 128, one workgroup per CU; wave = 32
+//     queries.  All waves of a workgroup share each K/V tile copied to LDS.
 //   * S^T = K Q^T is computed per 32-key group, so that a lane owns one
 //     query column and 16 of its scores: every per-query softmax quantity is
 //     lane-local (lanes l and l^32 share a query), and O^T = V^T P^T leaves the
@@ -22,14 +24,13 @@
 //     the tile's weight sum, which bounds its largest weight), so the common
 //     path spends one FMA and one v_exp_f32 per score and no max at all.  The
 //     result is exact softmax: out = (sum p v) / (sum p) with a common m.
-//   * The weights are rounded to bf16 for the PV product and summed from those
-//     rounded values (v_dot2_f32_bf16 against 1.0), so numerator and
-//     denominator see the same weights.
-//   * K and V^T tiles of 64 keys are double-buffered in LDS with an XOR
+//   * The weights are rounded to bf16 for the PV product; the row sums are
+//     taken in fp32 from the unrounded exponentials.
+//   * K and V^T tiles of 64 keys rotate through three LDS buffers with an XOR
 //     swizzle of 16-byte chunks (conflict-free ds_read_b128 for the MFMA
-//     operands).  The next tile streams from global memory straight into the
-//     other LDS buffer (global_load_lds_dwordx4, no staging registers) while
-//     the current tile computes.  One barrier per tile.
+//     operands).  The tile after next streams from global memory straight
+//     into a free buffer (global_load_lds_dwordx4, no staging registers)
+//     while the current tile computes.  One barrier per tile.
 //   * Workgroups are mapped to tasks XCD-major: the hardware deals workgroups
 //     round-robin to the 8 XCDs, so consecutive tasks (same block and head,
 //     neighbouring query tiles, hence the same K/V stream) share an XCD's L2.
@@ -117,23 +118,16 @@ struct WaveState {
   float l_sum;         // this lane's share of the weight sum
 };
 
-// Launch shape per head dim: waves per workgroup (32 queries each).  D = 64:
-// 4 waves, three workgroups per CU; D = 128: 8 waves sharing one set of LDS
-// buffers, one workgroup per CU.
+// Launch shape per head dim: waves per workgroup (32 queries each), one
+// workgroup per CU.  D = 64: 12 waves, 3 per SIMD; D = 128: 8 waves, 2 per
+// SIMD.  As many queries as the registers allow share each K/V tile copy.
 template <int D> struct Shape;
-#ifndef BA_NW64
-#define BA_NW64 12
-#endif
-template <> struct Shape<64> { static constexpr int NW = BA_NW64, WAVES_PER_SIMD = 3; };
+template <> struct Shape<64> { static constexpr int NW = 12, WAVES_PER_SIMD = 3; };
 template <> struct Shape<128> { static constexpr int NW = 8, WAVES_PER_SIMD = 2; };
 
 constexpr int kBuffers = 3;   // LDS tile buffers: in use, being consumed, being filled
-// a step's LDS operand reads issued ahead of their MFMA (D = 64: three waves
-// per SIMD hide the rest; D = 128: two waves, more reads in flight)
-#ifndef BA_LDS_AHEAD_128
-#define BA_LDS_AHEAD_128 3
-#endif
-template <int D> constexpr int kLdsAhead = D == 64 ? 2 : BA_LDS_AHEAD_128;
+// a step's LDS operand reads issued ahead of their MFMA
+template <int D> constexpr int kLdsAhead = 3;
 
 template <int D>
 struct Tile {
