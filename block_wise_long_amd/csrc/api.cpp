@@ -19,6 +19,12 @@ namespace {
 // tiles per task the split is 10-50 % slower than whole tasks, at 64 equal,
 // at the video key sets' ~170 faster).
 constexpr int kSplitMinTilesPerWg = 24;
+// ... and only when whole tasks would leave at least a quarter of an XCD's
+// resident slots idle in their last round (measured at the 480p block shape
+// with 16-96 heads: cutting tasks costs about a fifth of a round; with 1/8
+// of the slots idle whole tasks were 1.5 % faster, at 3/16 the two tied, at
+// 1/4 the split was 0.6 % faster).
+constexpr int64_t kSplitIdleNum = 1, kSplitIdleDen = 4;
 
 thread_local char g_err[512] = "";
 
@@ -380,8 +386,16 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
       const size_t pb = ba::attention_partial_bytes(D);
       int64_t tail = resident / 8;           // tail workgroups per XCD: one per resident slot
       const int64_t fit = (int64_t)(workspace_bytes / (16 * pb));
+      // whole tasks alone: the busiest XCD's last round leaves `idle` of its
+      // resident slots empty.  Cutting tasks costs about a fifth of a round
+      // (partial stores, merge launch), so a nearly full last round is left
+      // alone.
+      const int64_t slots = resident / 8;
+      const int64_t per_xcd = (tasks + 7) / 8;
+      const int64_t idle = (per_xcd + slots - 1) / slots * slots - per_xcd;
+      const bool worth = idle * kSplitIdleDen >= slots * kSplitIdleNum;
       if (tail > fit) tail = fit;
-      if (tail >= 1 && tasks >= 8 * tail) {
+      if (worth && tail >= 1 && tasks >= 8 * tail) {
         a.split = 1;
         a.tail_wg = (int32_t)tail;
         a.partials = static_cast<float*>(workspace);

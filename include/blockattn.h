@@ -154,7 +154,9 @@ typedef struct {
  *          a cut task are written there and folded by a second kernel on the
  *          same stream.  Without it (NULL) each query tile is one workgroup.
  *          The split is skipped when the pieces would be short (fewer than
- *          24 key tiles of 64 per tail workgroup, e.g. a text-only key set);
+ *          24 key tiles of 64 per tail workgroup, e.g. a text-only key set)
+ *          and when whole query tiles would leave less than a quarter of an
+ *          XCD's workgroup slots idle in their last round;
  *          ba_attention_plan tells which schedule a call takes.
  *          Results agree to rounding either way and are deterministic.  Its
  *          contents need no initialisation; calls that share a workspace must
