@@ -399,7 +399,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the shader clock ramps up over the first ~50 ms of sustained load: 200
+    # untimed steps (~0.1 s at the 480p block) reach the steady state that
+    # 1000 timed steps also hold
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=1, help="config index (1 is the default bench line)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
