@@ -122,8 +122,9 @@ struct WaveState {
 // workgroup per CU.  D = 64: 12 waves, 3 per SIMD; D = 128: 8 waves, 2 per
 // SIMD.  As many queries as the registers allow share each K/V tile copy.
 template <int D> struct Shape;
-template <> struct Shape<64> { static constexpr int NW = 12, WAVES_PER_SIMD = 3; };
-template <> struct Shape<128> { static constexpr int NW = 8, WAVES_PER_SIMD = 2; };
+// KW of the waves copy the K tile, the others the V^T tile (see load_tile).
+template <> struct Shape<64> { static constexpr int NW = 12, WAVES_PER_SIMD = 3, KW = 8; };
+template <> struct Shape<128> { static constexpr int NW = 8, WAVES_PER_SIMD = 2, KW = 4; };
 
 constexpr int kBuffers = 3;   // LDS tile buffers: in use, being consumed, being filled
 // a step's LDS operand reads issued ahead of their MFMA
@@ -138,8 +139,17 @@ struct Tile {
   static constexpr int K_CH = kKTile * KCH;          // chunks of the K tile
   static constexpr int V_CH = D * (kKTile / 8);      // chunks of the V^T tile
   static constexpr int CH = K_CH + V_CH;
-  static constexpr int LOADS = (CH + THREADS - 1) / THREADS;   // copy rounds per tile
-  static_assert(K_CH % 64 == 0 && CH % 64 == 0, "a wave's chunks are all K or all V");
+  static constexpr int LOADS = (CH + THREADS - 1) / THREADS;   // zero-fill rounds per buffer
+  // copies: KW waves take the K tile in KR rounds of 64 chunks, the other VW
+  // waves the V^T tile in VR rounds
+  static constexpr int KW = Shape<D>::KW, VW = NW - KW;
+  static constexpr int KR = K_CH / 64 / KW, VR = V_CH / 64 / VW;
+  static constexpr int K_ROWS_STEP = 64 * KW / KCH;  // K rows between a wave's rounds
+  static constexpr int V_DIMS_STEP = 8 * VW;         // V^T rows between a wave's rounds
+  static_assert(KW > 0 && VW > 0 && KR * KW * 64 == K_CH && VR * VW * 64 == V_CH, "copy rounds");
+  // a round's lanes keep the chunk (column) and row-order offsets of the first
+  // round: both swizzles and the row order repeat every 16 rows
+  static_assert(K_ROWS_STEP % 16 == 0 && V_DIMS_STEP % 16 == 0, "copy round strides");
 
   // XOR swizzle of the 16-byte chunks of a row.  A b128 LDS access is served
   // 8 lanes per 128 bytes or 16 lanes per 256 bytes of banks; consecutive
@@ -153,47 +163,64 @@ struct Tile {
   static __device__ __forceinline__ int v_idx(int d, int c) { return K_CH + d * 8 + (c ^ row_swz128(d)); }
 };
 
+// The per-lane part of a wave's copy address, the same for every tile and
+// round: a K wave's lane fetches chunk `lo` (in elements) of the K tile; a V
+// wave's lane fetches the chunk at column offset `lo` of V^T row `hi`, whose
+// pitch is the segment's T_pad.
+struct CopyLane {
+  unsigned lo, hi;
+};
+
+template <int D>
+__device__ __forceinline__ CopyLane copy_lane(int wave, int lane) {
+  using T = Tile<D>;
+  CopyLane cl;
+  if (wave < T::KW) {
+    const int p = wave * 64 + lane;               // LDS chunk of the first round
+    const int r = p / T::KCH, pos = p % T::KCH;
+    const int ch = D == 64 ? (pos ^ T::row_swz128(r)) : (pos ^ (r & 15));
+    cl.lo = (unsigned)(key_of_row(r) * D + ch * 8);
+    cl.hi = 0u;
+  } else {
+    const int pv = (wave - T::KW) * 64 + lane;    // V^T chunk of the first round
+    const int d = pv / 8, pos = pv % 8;
+    cl.lo = (unsigned)((pos ^ T::row_swz128(d)) * 8);
+    cl.hi = (unsigned)d;
+  }
+  return cl;
+}
+
 // Stream one K tile and one V^T tile straight from global memory into the LDS
 // buffer at byte address buf_lds (global_load_lds_dwordx4: lane i of a wave
-// fills the i-th 16 bytes after the wave's LDS base, held in M0).  The swizzle is applied by choosing which global
-// chunk each lane fetches for its fixed LDS position.  Completion is waited
+// fills the i-th 16 bytes after the wave's LDS base, held in M0).  The swizzle
+// is applied by choosing which global chunk each lane fetches for its fixed
+// LDS position.  Each wave copies K only or V^T only, so its lane offsets are
+// fixed (CopyLane, one multiply-add per tile for the V^T row pitch) and its
+// rounds differ by a uniform step of the base address.  Completion is waited
 // for with vmcnt before the barrier that publishes the buffer.
 template <int D>
-__device__ __forceinline__ void load_tile(const Cursor& c, int tid, unsigned buf_lds) {
+__device__ __forceinline__ void load_tile(const Cursor& c, const CopyLane& cl, int wave, unsigned buf_lds) {
   using T = Tile<D>;
-  const uint16_t* kb = c.k + (int64_t)c.off * D;   // uniform tile bases
-  const uint16_t* vb = c.v + c.off;
-  const int lane = tid & 63;
-  const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);   // uniform
+  const bool kw = wave < T::KW;                   // wave-uniform
+  const unsigned off = (cl.hi * (unsigned)c.tpad + cl.lo) * 2u;   // bytes, per lane
+  const uint16_t* base = kw ? c.k + (int64_t)c.off * D : c.v + c.off;
+  const int64_t step = kw ? (int64_t)T::K_ROWS_STEP * D : (int64_t)T::V_DIMS_STEP * c.tpad;
+  const unsigned lds0 = buf_lds + 16u * (unsigned)(kw ? wave * 64 : T::K_CH + (wave - T::KW) * 64);
+  const unsigned lds_step = 16u * 64u * (unsigned)(kw ? T::KW : T::VW);
+  const int rounds = kw ? T::KR : T::VR;
 #pragma unroll
-  for (int u = 0; u < T::LOADS; ++u) {
-    const int p0 = u * T::THREADS + wave_base;     // first LDS chunk of this wave
-    if (T::CH % T::THREADS != 0 && p0 >= T::CH) break;   // last round: fewer waves
-    const int p = p0 + lane;
-    const uint16_t* base;                          // uniform
-    unsigned idx;                                  // per lane, in elements
-    if (p0 < T::K_CH) {
-      const int r = p / T::KCH, pos = p % T::KCH;
-      const int ch = D == 64 ? (pos ^ T::row_swz128(r)) : (pos ^ (r & 15));
-      base = kb;
-      idx = (unsigned)(key_of_row(r) * D + ch * 8);
-    } else {
-      const int pv = p - T::K_CH;
-      const int d = pv / 8, pos = pv % 8;
-      const int ch = pos ^ T::row_swz128(d);
-      base = vb;
-      idx = (unsigned)(d * c.tpad + ch * 8);
-    }
-    // LDS byte address of this wave's first chunk (wave-uniform).  The copy
-    // is an asm statement: it has no register result and lands in LDS, which
-    // is read only after the explicit vmcnt wait and barrier that publish the
-    // buffer.  Seen by the compiler as an LDS write in flight, it would make
-    // every LDS read of the steps wait for all outstanding LDS reads.
-    const unsigned lds_base = buf_lds + 16u * (unsigned)(u * T::THREADS) +
-                              16u * (unsigned)wave_base;
+  for (int r = 0; r < (T::KR > T::VR ? T::KR : T::VR); ++r) {
+    if (r >= rounds) break;
+    // The copy is an asm statement: it has no register result and lands in
+    // LDS, which is read only after the explicit vmcnt wait and barrier that
+    // publish the buffer.  Seen by the compiler as an LDS write in flight, it
+    // would make every LDS read of the steps wait for all outstanding LDS
+    // reads.
+    const uint16_t* src = base + r * step;        // uniform
+    const unsigned lds = lds0 + (unsigned)r * lds_step;
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(idx * 2u), "s"(base), "s"(lds_base)
+                 : "v"(off), "s"(src), "s"(lds)
                  : "memory", "m0");
   }
 }
@@ -497,6 +524,8 @@ void attention_bf16_kernel(const AttnArgs a) {
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const CopyLane cl = copy_lane<D>(wave_u, lane);
   const float c = a.qscale;
 
   // one range of work: a whole task, or (split) a share of the XCD's tail
@@ -566,10 +595,10 @@ void attention_bf16_kernel(const AttnArgs a) {
       lc.off = rem * kKTile;
     }
     Cursor cc = lc;                           // cursor of the tile being consumed
-    load_tile<D>(lc, tid, lds_addr);
+    load_tile<D>(lc, cl, wave_u, lds_addr);
     if (n_tiles > 1) {
       advance<D>(a, B, h, lc);
-      load_tile<D>(lc, tid, lds_addr + 16u * T::CH);
+      load_tile<D>(lc, cl, wave_u, lds_addr + 16u * T::CH);
     }
     {
       // buffer 2 starts as zeros: the first step's deferred PV reads it
@@ -617,7 +646,7 @@ void attention_bf16_kernel(const AttnArgs a) {
         __syncthreads();
         if (t + 2 < n_tiles) {
           advance<D>(a, B, h, lc);
-          load_tile<D>(lc, tid, lds_addr + 16u * T::CH * pbuf);
+          load_tile<D>(lc, cl, wave_u, lds_addr + 16u * T::CH * pbuf);
         }
         advance<D>(a, B, h, cc);
       }
