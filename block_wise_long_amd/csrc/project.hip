@@ -70,35 +70,41 @@ __device__ __forceinline__ unsigned pack2(float lo, float hi) {
 // each, straight from global memory into LDS (global_load_lds_dwordx4 issued
 // from asm: no register result; the stage is read only after the vmcnt wait
 // and barrier that publish it).  Rows past the end are clamped to the last
-// row; their results are not stored.
-__device__ __forceinline__ void load_stage(const ProjArgs& a, const uint16_t* xb, int ch0, int t0, int k0,
-                                           int tid, unsigned stage_lds) {
+// row; their results are not stored.  A lane fetches the same rows and
+// chunks in every stage: its byte offsets (stage_offsets) are computed once
+// per tile, and a stage only moves the uniform base by its first input dim.
+__device__ __forceinline__ void stage_offsets(const ProjArgs& a, int ch0, int t0, int tid,
+                                              unsigned (&off)[kLoads]) {
   const int lane = tid & 63;
-  const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);
+  const int wave_base = tid & ~63;
 #pragma unroll
   for (int u = 0; u < kLoads; ++u) {
-    const int p0 = u * kThreads + wave_base;
-    const int p = p0 + lane;
-    const uint16_t* base;
-    unsigned off;
+    const int p = u * kThreads + wave_base + lane;
     if (u < kWLoads) {
       const int r = p / kRowChunks, c = (p % kRowChunks) ^ swz(r);
       int row = ch0 + r;
       row = row < a.n_ch ? row : a.n_ch - 1;
-      base = a.w;
-      off = (unsigned)(row * a.dim + k0 + 8 * c) * 2u;
+      off[u] = (unsigned)(row * a.dim + 8 * c) * 2u;
     } else {
       const int q = p - kWRows * kRowChunks;
       const int r = q / kRowChunks, c = (q % kRowChunks) ^ swz(r);
       int tok = t0 + r;
       tok = tok < a.n_tokens ? tok : a.n_tokens - 1;
-      base = xb;
-      off = (unsigned)(tok * a.dim + k0 + 8 * c) * 2u;
+      off[u] = (unsigned)(tok * a.dim + 8 * c) * 2u;
     }
-    const unsigned lds = stage_lds + 16u * (unsigned)p0;
+  }
+}
+
+__device__ __forceinline__ void load_stage(const ProjArgs& a, const uint16_t* xb, const unsigned (&off)[kLoads],
+                                           int k0, int tid, unsigned stage_lds) {
+  const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);
+#pragma unroll
+  for (int u = 0; u < kLoads; ++u) {
+    const uint16_t* base = (u < kWLoads ? a.w : xb) + k0;   // uniform
+    const unsigned lds = stage_lds + 16u * (unsigned)(u * kThreads + wave_base);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(off), "s"(base), "s"(lds)
+                 : "v"(off[u]), "s"(base), "s"(lds)
                  : "memory", "m0");
   }
 }
@@ -172,6 +178,8 @@ void project_kernel(const ProjArgs a) {
   const int t0 = tile.tt * kProjTokTile;
   const int ch0 = a.ch_begin + tile.ct * kProjChTile;
   const int n_k = a.dim / kKStep;
+  unsigned loff[kLoads];
+  stage_offsets(a, ch0, t0, tid, loff);
 
   f32x16 acc[kRB][kTB];
 #pragma unroll
@@ -188,7 +196,7 @@ void project_kernel(const ProjArgs a) {
   // so a wave's MFMA stream never waits on its own LDS reads.
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
-    if (s < n_k) load_stage(a, xb, ch0, t0, s * kKStep, tid, lds_addr + 16u * kStageChunks * s);
+    if (s < n_k) load_stage(a, xb, loff, s * kKStep, tid, lds_addr + 16u * kStageChunks * s);
   {
     const int issued = n_k < kStages - 1 ? n_k : kStages - 1;
     wait_newer(issued - 1);                             // stage 0 has landed
@@ -224,7 +232,7 @@ void project_kernel(const ProjArgs a) {
         wait_newer((ahead < n_k ? ahead : n_k - 1) - (kt + 1));
         __syncthreads();
         if (kt + kStages - 1 < n_k)
-          load_stage(a, xb, ch0, t0, (kt + kStages - 1) * kKStep, tid,
+          load_stage(a, xb, loff, (kt + kStages - 1) * kKStep, tid,
                      lds_addr + 16u * kStageChunks * ((kt + kStages - 1) % kStages));
         read_frag(nxt, lds[(kt + 1) % kStages], 0);
       }
