@@ -129,6 +129,12 @@ template <> struct Shape<128> { static constexpr int NW = 8, WAVES_PER_SIMD = 2,
 constexpr int kBuffers = 3;   // LDS tile buffers: in use, being consumed, being filled
 // a step's LDS operand reads issued ahead of their MFMA
 template <int D> constexpr int kLdsAhead = 3;
+// Where a step's weight computation goes.  D = 64 (VALU-bound, three waves
+// per SIMD): in chunks after the MFMAs, so every wave keeps both pipes busy.
+// D = 128 (two waves per SIMD, twice the MFMAs per weight): all of it after
+// the step's last MFMA, so that one wave's MFMA phase overlaps the other's
+// VALU phase (measured 4 % faster at the 720p block; the same at D = 64).
+template <int D> constexpr bool kSplitPhases = D == 128;
 
 template <int D>
 struct Tile {
@@ -331,10 +337,10 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
   }
   // ---- hot block: matrix cores and vector ALUs work side by side ----------
   // The wave issues in order, so the step is laid out by hand: each MFMA is
-  // followed by the LDS read of the operand two MFMAs ahead and by its share
-  // of the weight computation (one of eight chunks after every MFMA at
-  // D = 64, after every second one at D = 128); scheduling barriers keep the
-  // compiler from regrouping them.
+  // followed by the LDS read of the operand three MFMAs ahead and, at D = 64,
+  // by its share of the weight computation (one of eight chunks); at
+  // D = 128 the chunks all follow the last MFMA (kSplitPhases).  Scheduling
+  // barriers keep the compiler from regrouping them.
   float l_g;
   {
     // nothing of the LGKM counter is outstanding here: with that known, each
@@ -372,8 +378,9 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
         w.o[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], p[k2], w.o[ob], 0, 0, 0);
       }
       if (m + LA < NM) fr[m + LA] = operand(m + LA);
+      if (kSplitPhases<D> && m == NM - 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (; chunk < 8 && chunk * NM < 8 * (m + 1); ++chunk) {
+      for (; chunk < 8 && (kSplitPhases<D> ? m == NM - 1 : chunk * NM < 8 * (m + 1)); ++chunk) {
         const int k2 = chunk / 4, i = 2 * (chunk % 4);
         const float e0 = __builtin_amdgcn_exp2f(sc[8 * k2 + i]);
         const float e1 = __builtin_amdgcn_exp2f(sc[8 * k2 + i + 1]);
