@@ -203,11 +203,12 @@ def test_growing_scores_exercise_lazy_maximum(D):
     assert np.nanmax(np.abs(lse.cpu().numpy() - ref_lse) / np.maximum(1, np.abs(ref_lse))) < 1e-3
 
 
-def test_scores_far_below_zero_do_not_underflow():
+@pytest.mark.parametrize("D", [64, 128])
+def test_scores_far_below_zero_do_not_underflow(D):
     # every score around -1000 in the exp2 domain: the first tile sets the
     # reference maximum, so the weights stay normal
     rng = _rng(13)
-    H, D, L = 1, 64, 300
+    H, L = 1, 300
     w = Workload("bf16", 1, L, H, D, 0)
     k = np.zeros((L, H, D))
     k[..., 0] = -64.0
@@ -221,6 +222,28 @@ def test_scores_far_below_zero_do_not_underflow():
     out, _ = w.run(qb, metas, scale=1.0)
     ref, _ = w.oracle(qb, metas, scale=1.0)
     check_contract(decode(out, "bf16"), ref, "bf16", gate2=False)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_growing_scores_with_ragged_segments_and_text(D):
+    # the lazy maximum is raised inside tail groups (segments of 500 and 77
+    # keys, 40 text keys): masked keys must stay out of the new reference
+    rng = _rng(14 + D)
+    H = 2
+    w = Workload("bf16", 2, 512, H, D, 64)
+    for n, (lo, hi) in ((500, (0.05, 3.0)), (77, (3.0, 4.5))):
+        k = N.bf16_bits_to_f64(draw(rng, (n, H, D), 1.0, "bf16"))
+        kb = N.f64_to_bf16_bits(k * np.linspace(lo, hi, n)[:, None, None])
+        w.append(kb, draw(rng, (n, H, D), 1.0, "bf16"))
+    w.set_text(draw(rng, (40, H, D), 1.0, "bf16"), draw(rng, (40, H, D), 1.0, "bf16"))
+    q = draw(rng, (1, 130, H, D), 1.0, "bf16")
+    metas = [{"q_len": 130, "segs": [(0, 500), (1, 77)], "text_slot": 0, "text_len": 40}]
+    out, lse = w.run(q, metas, scale=0.5)
+    ref, ref_lse = w.oracle(q, metas, scale=0.5)
+    got = decode(out, "bf16")
+    check_contract(got, ref, "bf16", gate2=False)
+    assert np.nanmax(np.abs(got - ref)) <= 2 ** -6 * np.nanmax(np.abs(ref))
+    assert np.nanmax(np.abs(lse.cpu().numpy() - ref_lse) / np.maximum(1, np.abs(ref_lse))) < 1e-3
 
 
 def test_in_place_output():
