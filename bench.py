@@ -43,6 +43,13 @@ PROJ_SRC = (os.path.join(ROOT, "block_wise_long_amd", "csrc", "project.hip"),
 PROJ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "project_d64_qkv480p_traffic.md")
 
 
+def attention_kernel_name(B, D, max_keys):
+    """The bf16 attention kernel a launch takes: its launch shape (0 wide, 1
+    narrow) follows from the query tile the library reports for the key set."""
+    wide = B.ba_attention_query_tile(D, B.BA_BF16, 1 << 30)
+    return f"attention_bf16_kernel<{D}, {0 if B.ba_attention_query_tile(D, B.BA_BF16, max_keys) == wide else 1}>"
+
+
 def kernel_hash(src=ATTN_SRC):
     h = hashlib.sha256()
     for path in ((src,) if isinstance(src, str) else src):
@@ -386,7 +393,7 @@ def cross_bench(args):
                       "text_keys": TXT},
            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                        "kernel": f"attention_bf16_kernel<{D}>", "flop_per_launch": flops},
+                        "kernel": attention_kernel_name(B, D, TXT), "flop_per_launch": flops},
            # q and out cross HBM once each; text K/V are 3 MB
            "hbm_bytes_per_launch": 2 * L * H * D * 2 + 2 * TXT * H * D * 2,
            "self_only_ms": round(ms_self, 5),
@@ -569,7 +576,7 @@ def main():
                      "peak_per_clk_per_cu": EXP_PER_CLK_PER_CU},
         "roofline": {"bound": "mfma", "achieved": round(tflops_attn, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops_attn / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": f"attention_bf16_kernel<{D}>",
+                     "traffic": traffic, "kernel": attention_kernel_name(B, D, cfg.key_len),
                      "flop_per_launch": flops},
     }
     if args.cpu_budget > 0 and cfg.n_blocks == 1 and not cfg.full_sequence:

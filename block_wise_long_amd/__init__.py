@@ -75,7 +75,7 @@ _SIGS = {
                                   ctypes.POINTER(ba_block_meta), _I32, ctypes.c_float, _P, _P,
                                   _P, ctypes.c_size_t, _P]),
     "ba_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
-    "ba_attention_query_tile": (_I32, [_I32, _I32]),
+    "ba_attention_query_tile": (_I32, [_I32, _I32, _I32]),
     "ba_attention_plan": (_I32, [_I32, ctypes.POINTER(ba_ring), ctypes.POINTER(ba_ring),
                                  ctypes.POINTER(ba_block_meta), _I32, ctypes.c_size_t, ctypes.POINTER(_I32)]),
     "ba_block_update": (_I32, [_P, _P, _I64, ctypes.POINTER(_I32), _I32, ctypes.POINTER(ba_schedule), _P]),
@@ -246,9 +246,10 @@ def ba_attention_plan(q_stride, cache, text, metas, workspace_bytes):
     return tail.value
 
 
-def ba_attention_query_tile(head_dim, dtype):
-    """Queries of one head per workgroup of ba_block_attention (0: unsupported)."""
-    return _lib.ba_attention_query_tile(head_dim, dtype)
+def ba_attention_query_tile(head_dim, dtype, max_keys):
+    """Queries of one head per workgroup of ba_block_attention in a launch
+    whose longest key set has max_keys keys (0: unsupported)."""
+    return _lib.ba_attention_query_tile(head_dim, dtype, max_keys)
 
 
 def ba_attention_workspace_bytes(head_dim, dtype, n_blocks, q_stride, heads):

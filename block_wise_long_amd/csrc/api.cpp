@@ -130,12 +130,13 @@ void coefficients(const std::vector<double>& ab, int stride, int t, float* c1, f
   *c2 = (float)(sqrt(1.0 - ap) - sqrt(ap) * sqrt(1.0 - at) / sqrt(at));
 }
 
-// Workgroups of the bf16 attention kernel the current device holds at once.
-hipError_t resident_workgroups(int head_dim, int* n) {
+// Workgroups of the bf16 attention kernel (launch shape `shape`) the current
+// device holds at once.
+hipError_t resident_workgroups(int head_dim, int shape, int* n) {
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = ba::attention_bf16_resident(head_dim, &per_cu);
+  if (e == hipSuccess) e = ba::attention_bf16_resident(head_dim, shape, &per_cu);
   *n = e == hipSuccess ? cus * per_cu : 0;
   return e;
 }
@@ -244,9 +245,10 @@ ba_status ba_cache_append_batched(const ba_ring* ring, const void* k, const void
   return append_common(ring, k, v, n_tokens, slots, n_blocks, stream);
 }
 
-int32_t ba_attention_query_tile(int32_t head_dim, int32_t dtype) {
-  if (dtype == BA_BF16 && (head_dim == 64 || head_dim == 128)) return ba::attention_bf16_q_tile(head_dim);
-  if (dtype == BA_F32 && (head_dim == 64 || head_dim == 128)) return ba::attention_f32_q_tile();
+int32_t ba_attention_query_tile(int32_t head_dim, int32_t dtype, int32_t max_keys) {
+  if ((head_dim != 64 && head_dim != 128) || max_keys < 0) return 0;
+  if (dtype == BA_BF16) return ba::attention_bf16_q_tile(head_dim, ba::attention_bf16_shape(head_dim, max_keys));
+  if (dtype == BA_F32) return ba::attention_f32_q_tile();
   return 0;
 }
 
@@ -254,10 +256,16 @@ size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_b
                                     int32_t heads) {
   if (dtype != BA_BF16 || (head_dim != 64 && head_dim != 128) || n_blocks < 1 || q_stride < 1 || heads < 1)
     return 0;
-  int wg = 0;
-  if (resident_workgroups(head_dim, &wg) != hipSuccess || wg < 1) return 0;
-  // two partial results per tail workgroup, one tail workgroup per resident slot
-  return (size_t)2 * (wg / 8 * 8) * ba::attention_partial_bytes(head_dim);
+  // two partial results per tail workgroup, one tail workgroup per resident
+  // slot; enough for either launch shape
+  size_t bytes = 0;
+  for (int shape = 0; shape < (head_dim == 64 ? 2 : 1); ++shape) {
+    int wg = 0;
+    if (resident_workgroups(head_dim, shape, &wg) != hipSuccess || wg < 1) return 0;
+    const size_t b = (size_t)2 * (wg / 8 * 8) * ba::attention_partial_bytes(head_dim, shape);
+    if (b > bytes) bytes = b;
+  }
+  return bytes;
 }
 
 }  // extern "C"
@@ -293,6 +301,7 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
 
   // host-side segment tables (zero-length segments dropped, text last)
   std::vector<ba::AttnBlock> blocks(n_blocks);
+  std::vector<int64_t> block_keys(n_blocks, 0);
   int32_t q_max = 0;
   for (int b = 0; b < n_blocks; ++b) {
     const ba_block_meta& m = meta[b];
@@ -327,21 +336,26 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
       keys += m.text_len;
     }
     if (m.q_len > 0 && keys == 0) return fail(BA_ERR_INVALID_ARG, "block %d has queries but no keys", b);
+    block_keys[b] = m.q_len > 0 ? keys : 0;
     if (m.q_len > q_max) q_max = m.q_len;
   }
   if (n_blocks == 0 || q_max == 0) return ok();
 
   const bool bf16 = cache->dtype == BA_BF16;
-  const int qtile = bf16 ? ba::attention_bf16_q_tile(D) : ba::attention_f32_q_tile();
   const float sc = scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
   const int eb = elem_bytes(cache->dtype);
-  int resident = 0;   // workgroups the device holds at once (split schedule)
-  if (bf16 && has_workspace) {
-    hipError_t e = resident_workgroups(D, &resident);
-    if (e != hipSuccess) return hip_fail(e, "device query");
-  }
   for (int first = 0; first < n_blocks; first += ba::kAttnMaxBlocks) {
     const int nb = n_blocks - first < ba::kAttnMaxBlocks ? n_blocks - first : ba::kAttnMaxBlocks;
+    // launch shape from the launch's longest key set
+    int64_t max_keys = 0;
+    for (int i = 0; i < nb; ++i) max_keys = block_keys[first + i] > max_keys ? block_keys[first + i] : max_keys;
+    const int shape = bf16 ? ba::attention_bf16_shape(D, max_keys) : 0;
+    const int qtile = bf16 ? ba::attention_bf16_q_tile(D, shape) : ba::attention_f32_q_tile();
+    int resident = 0;   // workgroups the device holds at once (split schedule)
+    if (bf16 && has_workspace) {
+      hipError_t e = resident_workgroups(D, shape, &resident);
+      if (e != hipSuccess) return hip_fail(e, "device query");
+    }
     ba::AttnArgs a;
     memset(&a, 0, sizeof(a));
     int32_t qm = 0;
@@ -383,7 +397,7 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
     a.total_work = (int32_t)work;
     a.wg_per_xcd = (int32_t)((tasks + 7) / 8);   // default: one whole task per workgroup
     if (resident > 0) {
-      const size_t pb = ba::attention_partial_bytes(D);
+      const size_t pb = ba::attention_partial_bytes(D, shape);
       int64_t tail = resident / 8;           // tail workgroups per XCD: one per resident slot
       const int64_t fit = (int64_t)(workspace_bytes / (16 * pb));
       // whole tasks alone: the busiest XCD's last round leaves `idle` of its
@@ -425,7 +439,7 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
       if (a.tail_wg > *plan) *plan = a.tail_wg;
       continue;
     }
-    hipError_t e = bf16 ? ba::launch_attention_bf16(a, D, stream) : ba::launch_attention_f32(a, D, stream);
+    hipError_t e = bf16 ? ba::launch_attention_bf16(a, D, shape, stream) : ba::launch_attention_f32(a, D, stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
   }
   return ok();

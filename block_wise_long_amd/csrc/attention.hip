@@ -118,13 +118,16 @@ struct WaveState {
   float l_sum;         // this lane's share of the weight sum
 };
 
-// Launch shape per head dim: waves per workgroup (32 queries each), one
-// workgroup per CU.  D = 64: 12 waves, 3 per SIMD; D = 128: 8 waves, 2 per
-// SIMD.  As many queries as the registers allow share each K/V tile copy.
-template <int D> struct Shape;
-// KW of the waves copy the K tile, the others the V^T tile (see load_tile).
-template <> struct Shape<64> { static constexpr int NW = 12, WAVES_PER_SIMD = 3, KW = 8; };
-template <> struct Shape<128> { static constexpr int NW = 8, WAVES_PER_SIMD = 2, KW = 4; };
+// Launch shapes: waves per workgroup (32 queries each).  S = 0, the wide
+// shape: one workgroup per CU, as many queries as the registers allow sharing
+// each K/V tile copy; D = 64: 12 waves, 3 per SIMD; D = 128: 8 waves, 2 per
+// SIMD.  S = 1, the narrow shape for short key sets (D = 64 only): 4 waves,
+// three workgroups per CU, whose prologues and epilogues overlap.  KW of the
+// waves copy the K tile, the others the V^T tile (see load_tile).
+template <int D, int S = 0> struct Shape;
+template <> struct Shape<64, 0> { static constexpr int NW = 12, WAVES_PER_SIMD = 3, KW = 8; };
+template <> struct Shape<64, 1> { static constexpr int NW = 4, WAVES_PER_SIMD = 3, KW = 2; };
+template <> struct Shape<128, 0> { static constexpr int NW = 8, WAVES_PER_SIMD = 2, KW = 4; };
 
 constexpr int kBuffers = 3;   // LDS tile buffers: in use, being consumed, being filled
 // a step's LDS operand reads issued ahead of their MFMA
@@ -136,9 +139,10 @@ template <int D> constexpr int kLdsAhead = 3;
 // VALU phase (measured 4 % faster at the 720p block; the same at D = 64).
 template <int D> constexpr bool kSplitPhases = D == 128;
 
-template <int D>
+// Tile<D, S>: the LDS layout (the same for every shape) and the launch shape
+template <int D, int S = 0>
 struct Tile {
-  static constexpr int NW = Shape<D>::NW;
+  static constexpr int NW = Shape<D, S>::NW;
   static constexpr int THREADS = NW * 64;
   static constexpr int QTILE = NW * 32;
   static constexpr int KCH = D / 8;                  // 16-B chunks per K row
@@ -148,7 +152,7 @@ struct Tile {
   static constexpr int LOADS = (CH + THREADS - 1) / THREADS;   // zero-fill rounds per buffer
   // copies: KW waves take the K tile in KR rounds of 64 chunks, the other VW
   // waves the V^T tile in VR rounds
-  static constexpr int KW = Shape<D>::KW, VW = NW - KW;
+  static constexpr int KW = Shape<D, S>::KW, VW = NW - KW;
   static constexpr int KR = K_CH / 64 / KW, VR = V_CH / 64 / VW;
   static constexpr int K_ROWS_STEP = 64 * KW / KCH;  // K rows between a wave's rounds
   static constexpr int V_DIMS_STEP = 8 * VW;         // V^T rows between a wave's rounds
@@ -177,9 +181,9 @@ struct CopyLane {
   unsigned lo, hi;
 };
 
-template <int D>
+template <int D, int S>
 __device__ __forceinline__ CopyLane copy_lane(int wave, int lane) {
-  using T = Tile<D>;
+  using T = Tile<D, S>;
   CopyLane cl;
   if (wave < T::KW) {
     const int p = wave * 64 + lane;               // LDS chunk of the first round
@@ -204,9 +208,9 @@ __device__ __forceinline__ CopyLane copy_lane(int wave, int lane) {
 // fixed (CopyLane, one multiply-add per tile for the V^T row pitch) and its
 // rounds differ by a uniform step of the base address.  Completion is waited
 // for with vmcnt before the barrier that publishes the buffer.
-template <int D>
+template <int D, int S>
 __device__ __forceinline__ void load_tile(const Cursor& c, const CopyLane& cl, int wave, unsigned buf_lds) {
-  using T = Tile<D>;
+  using T = Tile<D, S>;
   const bool kw = wave < T::KW;                   // wave-uniform
   const unsigned off = (cl.hi * (unsigned)c.tpad + cl.lo) * 2u;   // bytes, per lane
   const uint16_t* base = kw ? c.k + (int64_t)c.off * D : c.v + c.off;
@@ -441,31 +445,31 @@ __device__ __forceinline__ Where locate(const AttnArgs& a, int pos) {
   return w;
 }
 
-template <int D>
+template <int D, int S>
 struct Partial {
   // [wave][o block][element][lane] accumulators, then [wave][lane] m, then l
-  static constexpr int NW = Shape<D>::NW;
+  static constexpr int NW = Shape<D, S>::NW;
   static constexpr int O_FLOATS = NW * (D / 32) * 16 * 64;
   static constexpr int FLOATS = O_FLOATS + 2 * NW * 64;
 };
 
-template <int D>
+template <int D, int S>
 __device__ __forceinline__ void store_partial(float* part, int wave, int lane, const WaveState<D>& w) {
   constexpr int NOB = D / 32;
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
     for (int i = 0; i < 16; ++i) part[((wave * NOB + ob) * 16 + i) * 64 + lane] = w.o[ob][i];
-  part[Partial<D>::O_FLOATS + wave * 64 + lane] = w.m_ref;
-  part[Partial<D>::O_FLOATS + Partial<D>::NW * 64 + wave * 64 + lane] = w.l_sum;
+  part[Partial<D, S>::O_FLOATS + wave * 64 + lane] = w.m_ref;
+  part[Partial<D, S>::O_FLOATS + Partial<D, S>::NW * 64 + wave * 64 + lane] = w.l_sum;
 }
 
 // w <- w merged with the partial result at `part` (same lanes, same queries).
-template <int D>
+template <int D, int S>
 __device__ __forceinline__ void merge_partial(const float* part, int wave, int lane, WaveState<D>& w) {
   constexpr int NOB = D / 32;
-  const float m2 = part[Partial<D>::O_FLOATS + wave * 64 + lane];
-  const float l2 = part[Partial<D>::O_FLOATS + Partial<D>::NW * 64 + wave * 64 + lane];
+  const float m2 = part[Partial<D, S>::O_FLOATS + wave * 64 + lane];
+  const float l2 = part[Partial<D, S>::O_FLOATS + Partial<D, S>::NW * 64 + wave * 64 + lane];
   const float m = fmaxf(w.m_ref, m2);
   // (the state being folded into starts at m = -inf: equal maxima scale by 1)
   const float a1 = w.m_ref == m ? 1.f : __builtin_amdgcn_exp2f(w.m_ref - m);
@@ -506,11 +510,11 @@ __device__ __forceinline__ void store_output(const AttnArgs& a, int b, int h, in
     a.lse[((int64_t)b * a.heads + h) * a.q_stride + qrow] = (w.m_ref + __log2f(l_tot)) * kLn2;
 }
 
-template <int D>
-__global__ __launch_bounds__(Tile<D>::THREADS)
-__attribute__((amdgpu_waves_per_eu(Shape<D>::WAVES_PER_SIMD, Shape<D>::WAVES_PER_SIMD)))
+template <int D, int S>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Tile<D, S>::THREADS)))
+__attribute__((amdgpu_waves_per_eu(Shape<D, S>::WAVES_PER_SIMD, Shape<D, S>::WAVES_PER_SIMD)))
 void attention_bf16_kernel(const AttnArgs a) {
-  using T = Tile<D>;
+  using T = Tile<D, S>;
   constexpr int NKS = D / 16;        // k-steps of the QK^T product
   constexpr int NOB = D / 32;        // 32-row blocks of O^T
   __shared__ u32x4 lds[kBuffers][T::CH];
@@ -532,7 +536,7 @@ void attention_bf16_kernel(const AttnArgs a) {
   const int half = lane >> 5;
   const int wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const CopyLane cl = copy_lane<D>(wave_u, lane);
+  const CopyLane cl = copy_lane<D, S>(wave_u, lane);
   const float c = a.qscale;
 
   // one range of work: a whole task, or (split) a share of the XCD's tail
@@ -602,10 +606,10 @@ void attention_bf16_kernel(const AttnArgs a) {
       lc.off = rem * kKTile;
     }
     Cursor cc = lc;                           // cursor of the tile being consumed
-    load_tile<D>(lc, cl, wave_u, lds_addr);
+    load_tile<D, S>(lc, cl, wave_u, lds_addr);
     if (n_tiles > 1) {
       advance<D>(a, B, h, lc);
-      load_tile<D>(lc, cl, wave_u, lds_addr + 16u * T::CH);
+      load_tile<D, S>(lc, cl, wave_u, lds_addr + 16u * T::CH);
     }
     {
       // buffer 2 starts as zeros: the first step's deferred PV reads it
@@ -653,7 +657,7 @@ void attention_bf16_kernel(const AttnArgs a) {
         __syncthreads();
         if (t + 2 < n_tiles) {
           advance<D>(a, B, h, lc);
-          load_tile<D>(lc, cl, wave_u, lds_addr + 16u * T::CH * pbuf);
+          load_tile<D, S>(lc, cl, wave_u, lds_addr + 16u * T::CH * pbuf);
         }
         advance<D>(a, B, h, cc);
       }
@@ -676,8 +680,8 @@ void attention_bf16_kernel(const AttnArgs a) {
       store_output<D>(a, b, h, qrow, row_ok, half, w);
     } else {
       // a cut task: the merge kernel combines the pieces after this launch
-      store_partial<D>(a.partials + ((int64_t)2 * (x * a.tail_wg + tail_j) + (first_chunk ? 0 : 1)) *
-                                        Partial<D>::FLOATS, wave, lane, w);
+      store_partial<D, S>(a.partials + ((int64_t)2 * (x * a.tail_wg + tail_j) + (first_chunk ? 0 : 1)) *
+                                        Partial<D, S>::FLOATS, wave, lane, w);
     }
     pos += n_tiles;
     first_chunk = false;
@@ -690,8 +694,8 @@ void attention_bf16_kernel(const AttnArgs a) {
 // workgroups cut is folded from its pieces (in workgroup order, so the result
 // does not depend on timing) and normalised.  Same wave/lane layout as the
 // main kernel, so each lane reads back exactly what it wrote.
-template <int D>
-__global__ __launch_bounds__(Tile<D>::THREADS) void attention_merge_kernel(const AttnArgs a) {
+template <int D, int S>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Tile<D, S>::THREADS))) void attention_merge_kernel(const AttnArgs a) {
   constexpr int NOB = D / 32;
   const int x = blockIdx.x & 7;
   const int u = blockIdx.x >> 3;
@@ -711,7 +715,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS) void attention_merge_kernel(const
   const int wave = tid >> 6;
   const int h = at.ti / B.nqt;
   const int qt = at.ti - h * B.nqt;
-  const int qrow = qt * Tile<D>::QTILE + wave * 32 + (lane & 31);
+  const int qrow = qt * Tile<D, S>::QTILE + wave * 32 + (lane & 31);
   WaveState<D> w;
 #pragma unroll
   for (int j = 0; j < NOB; ++j)
@@ -722,7 +726,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS) void attention_merge_kernel(const
   for (int oj = j_lo; oj <= j_hi; ++oj) {
     // the task opens tail workgroup oj's range (slot 0) or follows its first chunk (slot 1)
     const int slot = plan.tail0 + split_start(n_tail, a.tail_wg, oj) >= tstart ? 0 : 1;
-    merge_partial<D>(a.partials + ((int64_t)2 * (x * a.tail_wg + oj) + slot) * Partial<D>::FLOATS, wave,
+    merge_partial<D, S>(a.partials + ((int64_t)2 * (x * a.tail_wg + oj) + slot) * Partial<D, S>::FLOATS, wave,
                      lane, w);
   }
   store_output<D>(a, at.b, h, qrow, qrow < B.q_len, half, w);
@@ -812,33 +816,38 @@ __global__ __launch_bounds__(kF32QTile) void attention_f32_kernel(const AttnArgs
 
 }  // namespace
 
-int attention_bf16_q_tile(int head_dim) { return head_dim == 64 ? Tile<64>::QTILE : Tile<128>::QTILE; }
+// shape: 0 wide, 1 narrow (head_dim 64 only)
+int attention_bf16_q_tile(int head_dim, int shape) {
+  return head_dim == 128 ? Tile<128, 0>::QTILE : shape ? Tile<64, 1>::QTILE : Tile<64, 0>::QTILE;
+}
 int attention_f32_q_tile() { return kF32QTile; }
-int attention_bf16_threads(int head_dim) { return head_dim == 64 ? Tile<64>::THREADS : Tile<128>::THREADS; }
-size_t attention_partial_bytes(int head_dim) {
-  return sizeof(float) * (head_dim == 64 ? Partial<64>::FLOATS : Partial<128>::FLOATS);
+size_t attention_partial_bytes(int head_dim, int shape) {
+  return sizeof(float) *
+         (head_dim == 128 ? Partial<128, 0>::FLOATS : shape ? Partial<64, 1>::FLOATS : Partial<64, 0>::FLOATS);
 }
 
-hipError_t attention_bf16_resident(int head_dim, int* per_cu) {
-  if (head_dim == 64)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<64>, Tile<64>::THREADS, 0);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<128>, Tile<128>::THREADS, 0);
+hipError_t attention_bf16_resident(int head_dim, int shape, int* per_cu) {
+  if (head_dim == 128)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<128, 0>, Tile<128, 0>::THREADS, 0);
+  if (shape)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<64, 1>, Tile<64, 1>::THREADS, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<64, 0>, Tile<64, 0>::THREADS, 0);
 }
 
-hipError_t launch_attention_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid(8 * a.wg_per_xcd);
-  if (head_dim == 64)
-    hipLaunchKernelGGL(attention_bf16_kernel<64>, grid, dim3(Tile<64>::THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(attention_bf16_kernel<128>, grid, dim3(Tile<128>::THREADS), 0, s, a);
+namespace {
+template <int D, int S>
+hipError_t launch_shape(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((attention_bf16_kernel<D, S>), dim3(8 * a.wg_per_xcd), dim3(Tile<D, S>::THREADS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.split || a.merge_per_xcd == 0) return e;
-  const dim3 mgrid(8 * a.merge_per_xcd);
-  if (head_dim == 64)
-    hipLaunchKernelGGL(attention_merge_kernel<64>, mgrid, dim3(Tile<64>::THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(attention_merge_kernel<128>, mgrid, dim3(Tile<128>::THREADS), 0, s, a);
+  hipLaunchKernelGGL((attention_merge_kernel<D, S>), dim3(8 * a.merge_per_xcd), dim3(Tile<D, S>::THREADS), 0, s, a);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attention_bf16(const AttnArgs& a, int head_dim, int shape, hipStream_t s) {
+  if (head_dim == 128) return launch_shape<128, 0>(a, s);
+  return shape ? launch_shape<64, 1>(a, s) : launch_shape<64, 0>(a, s);
 }
 
 hipError_t launch_attention_f32(const AttnArgs& a, int head_dim, hipStream_t s) {

@@ -179,9 +179,13 @@ size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_b
                                     int32_t q_stride, int32_t heads);
 
 /* Queries of one head that one workgroup of ba_block_attention takes (its
- * query tile): a block of q_len queries is heads * ceil(q_len / tile) tasks.
- * 0 for a head_dim / dtype pair the call does not support.  Needs no device. */
-int32_t ba_attention_query_tile(int32_t head_dim, int32_t dtype);
+ * query tile) in a launch whose longest key set (cache segments + text) has
+ * max_keys keys: a block of q_len queries is heads * ceil(q_len / tile)
+ * tasks.  bf16, head_dim 64: 128 up to 3072 keys (short key sets, several
+ * workgroups per CU), else 384; head_dim 128: 256; fp32: 64.  A call covers
+ * its blocks in launches of up to 16.  0 for a head_dim / dtype pair the call
+ * does not support or max_keys < 0.  Needs no device. */
+int32_t ba_attention_query_tile(int32_t head_dim, int32_t dtype, int32_t max_keys);
 
 /* The schedule ba_block_attention would take for these arguments and a
  * workspace of workspace_bytes (0: none), without launching anything:

@@ -200,9 +200,15 @@ def test_workspace_bytes_without_device():
     # fp32 never uses one; with no device to size the grid, none is asked for
     # query tiles: whole waves of 32 queries (bf16), 64 (fp32); 0 when unsupported
     for d in (64, 128):
-        assert B.ba_attention_query_tile(d, B.BA_BF16) % 32 == 0 and B.ba_attention_query_tile(d, B.BA_BF16) >= 128
-        assert B.ba_attention_query_tile(d, B.BA_F32) == 64
-    assert B.ba_attention_query_tile(96, B.BA_BF16) == 0 and B.ba_attention_query_tile(64, 7) == 0
+        for keys in (0, 1, 512, 3072, 3073, 11026, 1 << 20):
+            t = B.ba_attention_query_tile(d, B.BA_BF16, keys)
+            assert t % 32 == 0 and t >= 128
+            assert B.ba_attention_query_tile(d, B.BA_F32, keys) == 64
+    # head dim 64: the narrow shape for short key sets, the wide one above 3072 keys
+    assert B.ba_attention_query_tile(64, B.BA_BF16, 3072) < B.ba_attention_query_tile(64, B.BA_BF16, 3073)
+    assert B.ba_attention_query_tile(128, B.BA_BF16, 3072) == B.ba_attention_query_tile(128, B.BA_BF16, 3073)
+    assert B.ba_attention_query_tile(96, B.BA_BF16, 64) == 0 and B.ba_attention_query_tile(64, 7, 64) == 0
+    assert B.ba_attention_query_tile(64, B.BA_BF16, -1) == 0
     assert B.ba_attention_workspace_bytes(64, B.BA_F32, 1, 128, 2) == 0
     assert B.ba_attention_workspace_bytes(96, B.BA_BF16, 1, 128, 2) == 0
     assert B.ba_attention_workspace_bytes(64, B.BA_BF16, 0, 128, 2) == 0
