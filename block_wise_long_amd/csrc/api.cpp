@@ -406,8 +406,8 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
       // alone.
       const int64_t slots = resident / 8;
       const int64_t per_xcd = (tasks + 7) / 8;
-      const int64_t idle = (per_xcd + slots - 1) / slots * slots - per_xcd;
-      const bool worth = idle * kSplitIdleDen >= slots * kSplitIdleNum;
+      const int64_t idle = slots >= 1 ? (per_xcd + slots - 1) / slots * slots - per_xcd : 0;
+      const bool worth = slots >= 1 && idle * kSplitIdleDen >= slots * kSplitIdleNum;
       if (tail > fit) tail = fit;
       if (worth && tail >= 1 && tasks >= 8 * tail) {
         a.split = 1;
