@@ -9,9 +9,11 @@
 // and the text-conditioning K/V.
 //
 // bf16 kernel (gfx950, v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//   * workgroup = one query tile of one (block, head): 12 waves (384 queries)
-//     at head dim 64, 8 waves (256) at 128, one workgroup per CU; wave = 32
-//     queries.  All waves of a workgroup share each K/V tile copied to LDS.
+//   * workgroup = one query tile of one (block, head); wave = 32 queries.
+//     All waves of a workgroup share each K/V tile copied to LDS.  Wide
+//     shape: 12 waves (384 queries) at head dim 64, 8 waves (256) at 128, one
+//     workgroup per CU; narrow shape for short key sets (head dim 64): 4
+//     waves, three workgroups per CU (see Shape).
 //   * S^T = K Q^T is computed per 32-key group, so that a lane owns one
 //     query column and 16 of its scores: every per-query softmax quantity is
 //     lane-local (lanes l and l^32 share a query), and O^T = V^T P^T leaves the
@@ -20,8 +22,8 @@
 //     maximum are applied to the fp32 scores by one FMA each, so the score
 //     error does not grow with the score's magnitude.
 //   * The running maximum is lazy: scores are taken relative to a reference m
-//     that is raised only when a tile's weights would exceed 2^12 (checked on
-//     the tile's weight sum, which bounds its largest weight), so the common
+//     that is raised only when a group's weights would exceed 2^12 (checked on
+//     the group's weight sum, which bounds its largest weight), so the common
 //     path spends one FMA and one v_exp_f32 per score and no max at all.  The
 //     result is exact softmax: out = (sum p v) / (sum p) with a common m.
 //   * The weights are rounded to bf16 for the PV product; the row sums are
@@ -52,7 +54,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKTile = kKeyTile;   // keys per LDS tile
-constexpr float kLazyThreshold = 4096.0f;   // 2^12: bound on a tile's weight sum
+constexpr float kLazyThreshold = 4096.0f;   // 2^12: bound on a group's weight sum
 constexpr float kLn2 = 0.693147180559945309f;
 
 
