@@ -284,3 +284,30 @@ def test_more_blocks_than_one_launch_takes(workspace):
     assert np.nanmax(np.abs(lse.cpu().numpy() - ref_lse)) < 2e-3
     for b in range(nb):        # rows past each q_len untouched
         assert np.isnan(got[b, metas[b]["q_len"]:]).all()
+
+
+@pytest.mark.parametrize("workspace", ["auto", None])
+def test_launches_of_one_call_take_different_shapes(workspace):
+    # 18 blocks at head dim 64: the first launch (16 blocks) has key sets of at
+    # most 3072 keys (narrow workgroups), the second (2 blocks) one of 3300
+    # (wide workgroups); one call, one workspace, every block against the oracle
+    import block_wise_long_amd as B
+    rng = _rng(22)
+    H, D, nb = 2, 64, 18
+    w = Workload("bf16", 3, 1650, H, D, 16)
+    _fill(w, rng, (1650, 1422, 1650), H, D, "bf16", 0.5, 16)
+    q = draw(rng, (nb, 200, H, D), 0.5, "bf16")
+    metas = []
+    for b in range(nb):
+        segs = [(1, 1422), (2, 1650)] if b < 16 else [(0, 1650), (2, 1650)]
+        metas.append({"q_len": 200 - (b % 3) * 37, "segs": segs, "text_slot": 0, "text_len": 0})
+    assert B.ba_attention_query_tile(D, B.BA_BF16, 1422 + 1650) < B.ba_attention_query_tile(D, B.BA_BF16, 3300)
+    out, lse = w.run(q, metas, workspace=workspace)
+    ref, ref_lse = w.oracle(q, metas)
+    got = decode(out, "bf16")
+    check_contract(got, ref, "bf16", gate2=False)
+    rms = math.sqrt(np.nanmean(ref ** 2))
+    assert np.nanmax(np.abs(got - ref)) <= 2 ** -7 * np.nanmax(np.abs(ref)) + 0.05 * rms
+    assert np.nanmax(np.abs(lse.cpu().numpy() - ref_lse)) < 2e-3
+    for b in range(nb):
+        assert np.isnan(got[b, metas[b]["q_len"]:]).all()
