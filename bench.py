@@ -1,20 +1,25 @@
 """Benchmark of the block-wise attention hot path on one MI355X.
 
-One step = one pass of the whole hot path over one queued block of the
-480p video-DiT workload (24 heads x 64, 5400 queries = 4 latent frames of
-30x45 tokens, keys = 5400 cached neighbouring-block + 5400 own + 226 text):
-  1. ba_cache_append   the block's K/V into its ring slot
-  2. ba_block_attention  queries over [cached block | own block | text]
-  3. ba_block_update   the block's latents, DDIM step at t = 500
-Inputs are seeded synthetic tensors (N(0,1)*0.5 bf16 for Q/K/V, N(0,1) for
-latents and noise) already resident in HBM when the timed region starts.
+One step = one pass of the whole hot path over the 8 queued blocks that one
+GPU holds (each block: 24 heads x 64, 5400 queries = 4 latent frames of 30x45
+tokens, keys = 5400 cached neighbouring-block + 5400 own + 226 text, its own
+ring slots in a 16-slot ring):
+  1. ba_cache_append_batched  the blocks' K/V into their ring slots
+  2. ba_block_attention       one launch: every block's queries over
+                              [cached neighbour | own block | text]
+  3. ba_block_update          every block's latents, DDIM step at its own
+                              timestep (1, 143, ..., 1000)
+`--workload N` runs the step on another bf16 workload instead.  Inputs are
+seeded synthetic tensors (N(0,1)*0.5 bf16 for Q/K/V, N(0,1) for latents and
+noise) already resident in HBM when the timed region starts.
 
 Prints one JSON line.  `value` is block-attention TFLOP/s over the whole
-step (algorithmic FLOPs 4*Lq*Lk*D*H over valid keys / step time).  The
-`roofline` object rates the attention kernel alone against the bf16 dense
-MFMA peak, from HIP events around each of its launches on the launch stream.
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
-workload.
+step (algorithmic FLOPs 4*Lq*Lk*D*H*n_blocks over valid keys / step time).
+The `roofline` object rates the attention kernel alone against the bf16
+dense MFMA peak, from HIP events around each of its launches on the launch
+stream.  `other_configs` times the attention of the other target workloads
+(the 480p and 720p blocks) alone, after the timed region.  `cpu_baseline`
+times the fp64 CPU oracle on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -34,7 +39,6 @@ PEAK_HBM_GBS = 8000.0
 CLOCK_GHZ, N_CU = 2.4, 256
 EXP_PER_CLK_PER_CU = 16        # v_exp_f32: a wave64 every 16 clocks on each of 4 SIMDs
 ATTN_SRC = os.path.join(ROOT, "block_wise_long_amd", "csrc", "attention.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_bf16_d64_dit480p_traffic.md")
 
 
 # the producer's tile shape lives in internal.h: both files key its counters
@@ -58,7 +62,7 @@ def kernel_hash(src=ATTN_SRC):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload_name, traffic_file=TRAFFIC_FILE, src=ATTN_SRC):
+def traffic_from_profile(workload_name, traffic_file, src=ATTN_SRC):
     """HBM bytes per launch from a committed counter summary, or None when it
     is missing or was taken on another version of the kernel's source."""
     if not os.path.exists(traffic_file):
@@ -72,41 +76,70 @@ def traffic_from_profile(workload_name, traffic_file=TRAFFIC_FILE, src=ATTN_SRC)
     return float(b.group(1))
 
 
+def _oracle_block(cfg, inputs, b):
+    """The oracle's ring model of block b's key set (one ring slot per
+    segment, in key order), its text ring and its meta."""
+    from oracle import ring as R
+    H, D = cfg.heads, cfg.head_dim
+    if cfg.full_sequence:
+        n = len(cfg.segs[0])
+        seg = cfg.segs[0][0][1]
+        ks = [inputs["k_cur"][0][i * seg:(i + 1) * seg] for i in range(n)]
+        vs = [inputs["v_cur"][0][i * seg:(i + 1) * seg] for i in range(n)]
+    else:
+        ks = [inputs["k_ctx"][b], inputs["k_cur"][b]]
+        vs = [inputs["v_ctx"][b], inputs["v_cur"][b]]
+    ring = R.RingModel(len(ks), max(k.shape[0] for k in ks), H, D, cfg.dtype)
+    for k, v in zip(ks, vs):
+        ring.append(k, v, k.shape[0])
+    text = R.RingModel(1, cfg.text_len, H, D, cfg.dtype)
+    text.append(inputs["k_text"], inputs["v_text"], cfg.text_len)
+    meta = {"q_len": cfg.q_len, "segs": [(i, k.shape[0]) for i, k in enumerate(ks)],
+            "text_slot": 0, "text_len": cfg.text_len}
+    return ring, text, meta
+
+
 def cpu_baseline(cfg, inputs, budget_s):
-    """The oracle, as it stands, on whole heads of the workload until the
-    time budget is used (at least one head)."""
+    """The oracle, as it stands, on the workload's own inputs: units of
+    (block, head, a quarter of the block's queries over all its keys), taken
+    in order until the time budget is used (at least one unit)."""
     from oracle import attention as A
     from oracle import numerics as N
-    from oracle import ring as R
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    ring = R.RingModel(cfg.n_slots, cfg.slot_tokens, cfg.heads, cfg.head_dim, cfg.dtype)
-    ring.append(inputs["k_ctx"][0], inputs["v_ctx"][0], cfg.ctx_len)
-    ring.append(inputs["k_cur"][0], inputs["v_cur"][0], cfg.cur_len)
-    text = R.RingModel(1, cfg.text_len, cfg.heads, cfg.head_dim, cfg.dtype)
-    text.append(inputs["k_text"], inputs["v_text"], cfg.text_len)
-    q = N.decode(inputs["q"], cfg.dtype)
-    meta = [{"q_len": cfg.q_len, "segs": list(cfg.segs[0]), "text_slot": 0, "text_len": cfg.text_len}]
-    t0 = time.perf_counter()
-    heads = 0
-    while heads < cfg.heads:
-        A.block_attention_ref(q, ring, text, meta, heads=[heads])
-        heads += 1
-        if time.perf_counter() - t0 >= budget_s:
+    chunk = -(-cfg.q_len // 4)
+    units = [(b, h, r0) for b in range(cfg.n_blocks) for h in range(cfg.heads)
+             for r0 in range(0, cfg.q_len, chunk)]
+    done, rows_done, setup_s, t_run = 0, 0, 0.0, 0.0
+    cur_b, ring, text, meta, q = None, None, None, None, None
+    for b, h, r0 in units:
+        if b != cur_b:
+            t_s = time.perf_counter()
+            ring, text, meta = _oracle_block(cfg, inputs, b)
+            q = N.decode(inputs["q"][b:b + 1], cfg.dtype)
+            cur_b = b
+            setup_s += time.perf_counter() - t_s
+        rows = list(range(r0, min(r0 + chunk, cfg.q_len)))
+        t0 = time.perf_counter()
+        A.block_attention_ref(q, ring, text, [meta], heads=[h], rows=rows)
+        t_run += time.perf_counter() - t0
+        done += 1
+        rows_done += len(rows)
+        if t_run >= budget_s:
             break
-    dt = time.perf_counter() - t0
-    flops = 4.0 * cfg.q_len * cfg.key_len * cfg.head_dim * heads
+    flops = 4.0 * rows_done * cfg.key_len * cfg.head_dim
     try:
         affinity = len(os.sched_getaffinity(0))
     except Exception:  # noqa: BLE001
         affinity = None
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} of {cfg.heads} heads, all {cfg.q_len} queries over all {cfg.key_len} keys, "
-                      f"fp64 numpy (BLAS dgemm), {dt:.1f} s wall",
-            "gflops_fp64": round(flops / dt / 1e9, 2), "os_cpu_count": os.cpu_count(),
+    return {"value": flops / t_run / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(units)} (block, head, {chunk}-query chunk) units of {cfg.name} "
+                      f"({rows_done} query rows, each over all {cfg.key_len} keys), fp64 numpy "
+                      f"(BLAS dgemm), {t_run:.1f} s wall in the oracle call",
+            "gflops_fp64": round(flops / t_run / 1e9, 2), "os_cpu_count": os.cpu_count(),
             "sched_affinity": affinity, "blas_threads": threads}
 
 
@@ -148,6 +181,142 @@ def update_size_sweep(B, torch, sizes_mb=(16, 64, 256, 1024, 2048), reps=5):
         out.append({"MB": round(6.0 * n / 1e6, 1), "ms": round(ms, 4), "GBs": round(6.0 * n / (ms * 1e-3) / 1e9, 1)})
         del x, eps
     del flush
+    return out
+
+
+def traffic_file(cfg):
+    """Committed counter summary of the attention kernel on this workload."""
+    return os.path.join(ROOT, "profiles", f"attention_bf16_d{cfg.head_dim}_{cfg.name}_traffic.md")
+
+
+def warm_up(torch, fn, n_min, min_s):
+    """Untimed warm-up: at least n_min calls, continued until min_s seconds of
+    load have passed (the shader clock ramps up over tens of milliseconds of
+    sustained work).  Returns (calls run, seconds)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < n_min or time.perf_counter() - t0 < min_s:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
+class Workload:
+    """A workload's inputs on the device: the ring with every block's cached
+    context (written by the previous step), the text ring, q, out, the metas,
+    the blocks' own K/V to append each step, and (optionally) the latents."""
+
+    def __init__(self, B, torch, cfg, with_update=False):
+        from workloads import make_attention_inputs, make_update_inputs
+        self.B, self.cfg = B, cfg
+        inputs = make_attention_inputs(cfg)
+        self.inputs = inputs
+
+        def dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+        H, D = cfg.heads, cfg.head_dim
+        self.ring = B.ba_ring_init(cfg.n_slots, cfg.slot_tokens, H, D, B.BA_BF16)
+        self.text = B.ba_ring_init(1, cfg.text_len, H, D, B.BA_BF16)
+        B.ba_cache_append(self.text, dev(inputs["k_text"]), dev(inputs["v_text"]), cfg.text_len)
+        if cfg.full_sequence:
+            # the whole prefix is the block's own keys, one ring slot per 4-frame block
+            nseg = len(cfg.segs[0])
+            seg_len = cfg.segs[0][0][1]
+            self.k_cur = dev(inputs["k_cur"]).view(nseg, seg_len, H, D)
+            self.v_cur = dev(inputs["v_cur"]).view(nseg, seg_len, H, D)
+            self.cur_slots = [sl for sl, _ in cfg.segs[0]]
+        else:
+            B.ba_cache_append_batched(self.ring, dev(inputs["k_ctx"]), dev(inputs["v_ctx"]),
+                                      [sg[0][0] for sg in cfg.segs])
+            self.k_cur = dev(inputs["k_cur"])      # [n_blocks][L][H][D]
+            self.v_cur = dev(inputs["v_cur"])
+            self.cur_slots = [sg[1][0] for sg in cfg.segs]
+        self.q = dev(inputs["q"])
+        self.out = torch.empty_like(self.q)
+        self.metas = [B.make_meta(cfg.q_len, list(cfg.segs[b]), 0, cfg.text_len) for b in range(cfg.n_blocks)]
+        self.appended_tokens = self.k_cur.shape[0] * self.k_cur.shape[1]
+        # the cached context is in place: from here on a step appends the blocks' own K/V
+        B.ba_cache_append_batched(self.ring, self.k_cur, self.v_cur, self.cur_slots)
+        if with_update:
+            upd = make_update_inputs(cfg, inputs["_rng"])
+            self.x = dev(upd["x"])
+            self.eps = dev(upd["eps"])
+            self.ts = [int(t) for t in upd["t"]]
+        torch.cuda.synchronize()
+
+    def append(self):
+        self.B.ba_cache_append_batched(self.ring, self.k_cur, self.v_cur, self.cur_slots)
+
+    def attention(self):
+        self.B.ba_block_attention(self.q, self.ring, self.text, self.metas, out=self.out)
+
+    def release(self):
+        """Free the device buffers (the host inputs stay for the oracle)."""
+        for name in ("ring", "text", "k_cur", "v_cur", "q", "out", "x", "eps"):
+            if hasattr(self, name):
+                delattr(self, name)
+
+
+def attention_alone(B, torch, cfg, steps, warmup, min_s):
+    """ba_block_attention alone on a workload: mean/median/p10/p90 of `steps`
+    calls, HIP events on the launch stream around each call."""
+    w = Workload(B, torch, cfg)
+    stream = torch.cuda.current_stream()
+    n_warm, s_warm = warm_up(torch, w.attention, warmup, min_s)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        w.attention()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    w.release()
+    del w
+    torch.cuda.empty_cache()
+    mean = float(np.mean(ms))
+    tf = cfg.flops() / (mean * 1e-3) / 1e12
+    return {"n_blocks": cfg.n_blocks, "heads": cfg.heads, "head_dim": cfg.head_dim, "queries": cfg.q_len,
+            "keys": cfg.key_len, "calls": steps, "warmup_calls_run": n_warm, "warmup_s": round(s_warm, 3),
+            "attention_ms": round(mean, 5), "attention_median": round(float(np.median(ms)), 5),
+            "attention_p10": round(float(np.percentile(ms, 10)), 5),
+            "attention_p90": round(float(np.percentile(ms, 90)), 5),
+            "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "latent_frames_per_s": round(cfg.latent_frames / (mean * 1e-3), 1),
+            "kernel": attention_kernel_name(B, cfg.head_dim, cfg.key_len)}
+
+
+def append_size_sweep(B, torch, sizes_mb=(16, 64, 256, 1024, 2048), reps=5):
+    """ba_cache_append alone at growing sizes (bytes moved = K and V read
+    plus K and V written, 24 heads x 64), with a 512 MB write between calls
+    so that no call finds its source in the 256 MB Infinity Cache."""
+    H, D = 24, 64
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = []
+    for mb in sizes_mb:
+        n = max((mb << 20) // (4 * H * D * 2) // 64 * 64, 64)   # tokens: 2 tensors x (read + write)
+        k = torch.randn((n, H, D), device="cuda").to(torch.bfloat16)
+        v = torch.randn((n, H, D), device="cuda").to(torch.bfloat16)
+        ring = B.ba_ring_init(1, n, H, D, B.BA_BF16)
+        times = []
+        for _ in range(reps):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            B.ba_cache_append_batched(ring, k.view(1, n, H, D), v.view(1, n, H, D), [0])
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        moved = 4.0 * n * H * D * 2
+        out.append({"MB": round(moved / 1e6, 1), "ms": round(ms, 4), "GBs": round(moved / (ms * 1e-3) / 1e9, 1)})
+        del k, v, ring
+    del flush
+    torch.cuda.empty_cache()
     return out
 
 
@@ -406,11 +575,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the shader clock ramps up over the first ~50 ms of sustained load: 200
-    # untimed steps (~0.1 s at the 480p block) reach the steady state that
-    # 1000 timed steps also hold
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", type=int, default=1, help="config index (1 is the default bench line)")
+    ap.add_argument("--warmup", type=int, default=5)
+    # the shader clock ramps up over the first tens of milliseconds of
+    # sustained load: the warm-up runs at least this long, whatever --warmup says
+    ap.add_argument("--warmup-min-s", type=float, default=0.3)
+    ap.add_argument("--workload", type=int, default=3,
+                    help="config index of the step (3, the 8 queued blocks, is the default bench line)")
+    ap.add_argument("--also", type=lambda t: [int(x) for x in t.split(",") if x], default=[1, 2],
+                    help="config indices whose attention is also timed alone (comma list, empty: none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -458,64 +630,33 @@ def main():
 
     import torch
     import block_wise_long_amd as B
-    from workloads import CONFIGS, make_attention_inputs, make_update_inputs
+    from workloads import CONFIGS
 
     cfg = CONFIGS[args.workload]
     if cfg.dtype != "bf16":
         print(json.dumps({"error": "bench steps cover the bf16 workloads (1-4)"}))
         sys.exit(2)
     torch.cuda.set_device(0)
-    inputs = make_attention_inputs(cfg)
-    upd = make_update_inputs(cfg, inputs["_rng"])
-
-    def dev(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
-
+    w = Workload(B, torch, cfg, with_update=True)
     H, D = cfg.heads, cfg.head_dim
-    ring = B.ba_ring_init(cfg.n_slots, cfg.slot_tokens, H, D, B.BA_BF16)
-    text = B.ba_ring_init(1, cfg.text_len, H, D, B.BA_BF16)
-    B.ba_cache_append(text, dev(inputs["k_text"]), dev(inputs["v_text"]), cfg.text_len)
-    if cfg.full_sequence:
-        # the whole prefix is the block's own keys, one ring slot per 4-frame block
-        nseg = len(cfg.segs[0])
-        seg_len = cfg.segs[0][0][1]
-        k_cur = dev(inputs["k_cur"]).view(nseg, seg_len, H, D)
-        v_cur = dev(inputs["v_cur"]).view(nseg, seg_len, H, D)
-        cur_slots = [sl for sl, _ in cfg.segs[0]]
-    else:
-        # the neighbouring blocks' cached K/V were written by the previous step
-        B.ba_cache_append_batched(ring, dev(inputs["k_ctx"]), dev(inputs["v_ctx"]),
-                                  [sg[0][0] for sg in cfg.segs])
-        k_cur = dev(inputs["k_cur"])      # [n_blocks][L][H][D]
-        v_cur = dev(inputs["v_cur"])
-        cur_slots = [sg[1][0] for sg in cfg.segs]
-    q = dev(inputs["q"])
-    out = torch.empty_like(q)
-    x = dev(upd["x"])
-    eps = dev(upd["eps"])
-    ts = [int(t) for t in upd["t"]]
-    metas = [B.make_meta(cfg.q_len, list(cfg.segs[b]), 0, cfg.text_len) for b in range(cfg.n_blocks)]
     stream = torch.cuda.current_stream()
-    appended_tokens = k_cur.shape[0] * k_cur.shape[1]
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        B.ba_cache_append_batched(ring, k_cur, v_cur, cur_slots)
+        w.append()
         if ev is not None:
             ev[1].record(stream)
-        B.ba_block_attention(q, ring, text, metas, out=out)
+        w.attention()
         if ev is not None:
             ev[2].record(stream)
-        B.ba_block_update(x, eps, ts)
+        B.ba_block_update(w.x, w.eps, w.ts)
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_steps, warm_s = warm_up(torch, step, args.warmup, args.warmup_min_s)
 
-    # timed region: whole steps, bracketed by synchronisation
+    # timed region: exactly `steps` whole steps, bracketed by synchronisation
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -530,15 +671,23 @@ def main():
     ms_attn_all = [e[1].elapsed_time(e[2]) for e in evs]
     ms_attn = float(np.mean(ms_attn_all))
     ms_update = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    w.release()
+
+    # the other target configurations, attention alone, after the timed region
+    others = {}
+    for i in args.also:
+        if i == args.workload or CONFIGS[i].dtype != "bf16":
+            continue
+        others[CONFIGS[i].name] = attention_alone(B, torch, CONFIGS[i], args.steps, args.warmup, args.warmup_min_s)
 
     update_sweep = update_size_sweep(B, torch)
+    append_sweep = append_size_sweep(B, torch)
 
     flops = float(cfg.flops())
     tflops_step = flops / (ms_step * 1e-3) / 1e12
     tflops_attn = flops / (ms_attn * 1e-3) / 1e12
-    append_bytes = 2.0 * 2 * appended_tokens * H * D * 2    # read K,V + write K,V (valid tokens)
+    append_bytes = 2.0 * 2 * w.appended_tokens * H * D * 2    # read K,V + write K,V (valid tokens)
     update_bytes = 3.0 * cfg.update_elems * cfg.n_blocks * 2
-    traffic = traffic_from_profile(cfg.name)
     exps = float(cfg.n_blocks) * H * cfg.q_len * cfg.key_len
 
     res = {
@@ -558,6 +707,10 @@ def main():
                    "queries": cfg.q_len, "keys": cfg.key_len,
                    "key_segments": [cfg.ctx_len, cfg.cur_len, cfg.text_len],
                    "latent_frames_per_step": cfg.latent_frames},
+        # untimed warm-up actually run: the steps asked for, continued until
+        # the shader clock has had warmup_min_s of load to ramp up
+        "warmup_steps_run": warm_steps,
+        "warmup_s": round(warm_s, 3),
         "pct_bf16_peak_step": round(100 * tflops_step / PEAK_BF16_TFLOPS, 2),
         "latent_frames_per_s": round(cfg.latent_frames / (ms_step * 1e-3), 1),
         "kernel_ms": {"append": round(ms_append, 5), "attention": round(ms_attn, 5),
@@ -566,21 +719,26 @@ def main():
                       "attention_p90": round(float(np.percentile(ms_attn_all, 90)), 5),
                       "update": round(ms_update, 5)},
         "latent_frames_per_s_24_heads": round(cfg.latent_frames / (ms_step * 1e-3) * H / 24, 1),
-        "append_GBs": round(append_bytes / (ms_append * 1e-3) / 1e9, 1),
+        "other_configs": others,
+        # in the step the same blocks are appended every time, so the append
+        # reads from the 256 MB Infinity Cache; append_sweep is the HBM figure
+        "append_GBs_in_step": round(append_bytes / (ms_append * 1e-3) / 1e9, 1),
+        "append_sweep": append_sweep,
         "update_GBs": round(update_bytes / (ms_update * 1e-3) / 1e9, 1),
         "update_sweep": update_sweep,
         # the softmax's second bound: one exponential per (query, valid key,
-        # head); v_exp_f32 issues at a quarter rate, 16 per clock per CU
+        # head) against v_exp_f32's issue rate
         "exp_rate": {"exps_per_launch": exps,
                      "per_clk_per_cu": round(exps / (ms_attn * 1e-3) / (CLOCK_GHZ * 1e9) / N_CU, 3),
                      "peak_per_clk_per_cu": EXP_PER_CLK_PER_CU},
         "roofline": {"bound": "mfma", "achieved": round(tflops_attn, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops_attn / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": attention_kernel_name(B, D, cfg.key_len),
+                     "traffic": traffic_from_profile(cfg.name, traffic_file(cfg)),
+                     "kernel": attention_kernel_name(B, D, cfg.key_len),
                      "flop_per_launch": flops},
     }
-    if args.cpu_budget > 0 and cfg.n_blocks == 1 and not cfg.full_sequence:
-        res["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_budget)
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(cfg, w.inputs, args.cpu_budget)
         res["cpu_baseline"]["gpu_over_oracle"] = round(tflops_attn / res["cpu_baseline"]["value"], 1)
     else:
         res["cpu_baseline"] = None

@@ -16,9 +16,7 @@ import re
 import torch  # noqa: F401  (load order matters, see above)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# BLOCKATTN_LIB selects another build of the library (e.g. a variant built
-# with different compile options); by default the in-tree build is loaded.
-LIB_PATH = os.environ.get("BLOCKATTN_LIB") or os.path.join(_HERE, "libblockattn.so")
+LIB_PATH = os.path.join(_HERE, "libblockattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "blockattn.h")
 
 if not os.path.exists(LIB_PATH):
@@ -260,13 +258,14 @@ _WORKSPACES = {}
 
 
 def attention_workspace(head_dim, dtype, n_blocks, q_stride, heads, device=None):
-    """A workspace for ba_block_attention, cached per device and size.  Calls
-    that share it must be ordered on one stream.  None when none is used."""
+    """A workspace for ba_block_attention, cached per (device, stream, size):
+    calls on one stream are ordered and may share it, calls on different
+    streams get different buffers.  None when none is used."""
     nbytes = ba_attention_workspace_bytes(head_dim, dtype, n_blocks, q_stride, heads)
     if nbytes == 0:
         return None
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    key = (dev, nbytes)
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream, nbytes)
     ws = _WORKSPACES.get(key)
     if ws is None:
         ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)

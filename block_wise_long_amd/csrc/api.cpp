@@ -272,6 +272,47 @@ size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_b
 
 namespace {
 
+// Block b's segment table for the kernels: zero-length segments dropped, the
+// text last (slot -1 - text_slot).  *keys receives the block's key count (0
+// for a block without queries).  The checks of one meta entry.
+ba_status block_table(const ba_block_meta& m, int b, int32_t q_stride, const ba_ring* cache, const ba_ring* text,
+                      ba::AttnBlock* out, int64_t* keys_out) {
+  ba::AttnBlock& B = *out;
+  memset(&B, 0, sizeof(B));
+  if (m.q_len < 0 || m.q_len > q_stride)
+    return fail(BA_ERR_OUT_OF_RANGE, "block %d: q_len %d outside [0, %d]", b, m.q_len, q_stride);
+  if (m.n_segs < 0 || m.n_segs > BA_MAX_SEGS)
+    return fail(BA_ERR_OUT_OF_RANGE, "block %d: n_segs %d outside [0, %d]", b, m.n_segs, BA_MAX_SEGS);
+  B.q_len = m.q_len;
+  int64_t keys = 0;
+  for (int i = 0; i < m.n_segs; ++i) {
+    const ba_seg& sg = m.seg[i];
+    if (sg.slot < 0 || sg.slot >= cache->n_slots)
+      return fail(BA_ERR_OUT_OF_RANGE, "block %d seg %d: slot %d outside [0, %d)", b, i, sg.slot, cache->n_slots);
+    if (sg.len < 0 || sg.len > cache->slot_tokens)
+      return fail(BA_ERR_OUT_OF_RANGE, "block %d seg %d: len %d outside [0, %d]", b, i, sg.len, cache->slot_tokens);
+    if (sg.len == 0) continue;
+    B.slot[B.n_segs] = sg.slot;
+    B.len[B.n_segs] = sg.len;
+    ++B.n_segs;
+    keys += sg.len;
+  }
+  if (m.text_len != 0) {
+    if (text == nullptr) return fail(BA_ERR_INVALID_ARG, "text_len > 0 but text ring is NULL");
+    if (m.text_len < 0 || m.text_len > text->slot_tokens)
+      return fail(BA_ERR_OUT_OF_RANGE, "block %d: text_len %d outside [0, %d]", b, m.text_len, text->slot_tokens);
+    if (m.text_slot < 0 || m.text_slot >= text->n_slots)
+      return fail(BA_ERR_OUT_OF_RANGE, "block %d: text_slot %d outside [0, %d)", b, m.text_slot, text->n_slots);
+    B.slot[B.n_segs] = -1 - m.text_slot;
+    B.len[B.n_segs] = m.text_len;
+    ++B.n_segs;
+    keys += m.text_len;
+  }
+  if (m.q_len > 0 && keys == 0) return fail(BA_ERR_INVALID_ARG, "block %d has queries but no keys", b);
+  *keys_out = m.q_len > 0 ? keys : 0;
+  return BA_OK;
+}
+
 // The work of ba_block_attention after the pointer checks.  With plan != NULL
 // nothing is launched: *plan receives the most tail workgroups per XCD any of
 // the call's launches would use (0: every workgroup runs whole tasks).
@@ -298,46 +339,24 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
   const int D = cache->head_dim;
   const int H = cache->heads;
   if ((int64_t)n_blocks * q_stride * H > (int64_t)1 << 40) return fail(BA_ERR_OUT_OF_RANGE, "q too large");
+  // the bf16 kernel's per-lane copy offsets within a ring matrix are 32-bit
+  if (cache->dtype == BA_BF16) {
+    if (cache->slot_stride_tokens >= ba::kAttnMaxSlotStride)
+      return fail(BA_ERR_OUT_OF_RANGE, "cache slot stride %d tokens >= %lld (bf16 attention limit)",
+                  cache->slot_stride_tokens, (long long)ba::kAttnMaxSlotStride);
+    if (text != nullptr && text->slot_stride_tokens >= ba::kAttnMaxSlotStride)
+      return fail(BA_ERR_OUT_OF_RANGE, "text slot stride %d tokens >= %lld (bf16 attention limit)",
+                  text->slot_stride_tokens, (long long)ba::kAttnMaxSlotStride);
+  }
 
-  // host-side segment tables (zero-length segments dropped, text last)
-  std::vector<ba::AttnBlock> blocks(n_blocks);
-  std::vector<int64_t> block_keys(n_blocks, 0);
+  // every block's segment table is checked before anything is launched
   int32_t q_max = 0;
   for (int b = 0; b < n_blocks; ++b) {
-    const ba_block_meta& m = meta[b];
-    ba::AttnBlock& B = blocks[b];
-    memset(&B, 0, sizeof(B));
-    if (m.q_len < 0 || m.q_len > q_stride)
-      return fail(BA_ERR_OUT_OF_RANGE, "block %d: q_len %d outside [0, %d]", b, m.q_len, q_stride);
-    if (m.n_segs < 0 || m.n_segs > BA_MAX_SEGS)
-      return fail(BA_ERR_OUT_OF_RANGE, "block %d: n_segs %d outside [0, %d]", b, m.n_segs, BA_MAX_SEGS);
-    B.q_len = m.q_len;
+    ba::AttnBlock B;
     int64_t keys = 0;
-    for (int i = 0; i < m.n_segs; ++i) {
-      const ba_seg& sg = m.seg[i];
-      if (sg.slot < 0 || sg.slot >= cache->n_slots)
-        return fail(BA_ERR_OUT_OF_RANGE, "block %d seg %d: slot %d outside [0, %d)", b, i, sg.slot, cache->n_slots);
-      if (sg.len < 0 || sg.len > cache->slot_tokens)
-        return fail(BA_ERR_OUT_OF_RANGE, "block %d seg %d: len %d outside [0, %d]", b, i, sg.len, cache->slot_tokens);
-      if (sg.len == 0) continue;
-      B.slot[B.n_segs] = sg.slot;
-      B.len[B.n_segs] = sg.len;
-      ++B.n_segs;
-      keys += sg.len;
-    }
-    if (m.text_len != 0) {
-      if (m.text_len < 0 || m.text_len > text->slot_tokens)
-        return fail(BA_ERR_OUT_OF_RANGE, "block %d: text_len %d outside [0, %d]", b, m.text_len, text->slot_tokens);
-      if (m.text_slot < 0 || m.text_slot >= text->n_slots)
-        return fail(BA_ERR_OUT_OF_RANGE, "block %d: text_slot %d outside [0, %d)", b, m.text_slot, text->n_slots);
-      B.slot[B.n_segs] = -1 - m.text_slot;
-      B.len[B.n_segs] = m.text_len;
-      ++B.n_segs;
-      keys += m.text_len;
-    }
-    if (m.q_len > 0 && keys == 0) return fail(BA_ERR_INVALID_ARG, "block %d has queries but no keys", b);
-    block_keys[b] = m.q_len > 0 ? keys : 0;
-    if (m.q_len > q_max) q_max = m.q_len;
+    st = block_table(meta[b], b, q_stride, cache, text, &B, &keys);
+    if (st != BA_OK) return st;
+    if (meta[b].q_len > q_max) q_max = meta[b].q_len;
   }
   if (n_blocks == 0 || q_max == 0) return ok();
 
@@ -346,9 +365,15 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
   const int eb = elem_bytes(cache->dtype);
   for (int first = 0; first < n_blocks; first += ba::kAttnMaxBlocks) {
     const int nb = n_blocks - first < ba::kAttnMaxBlocks ? n_blocks - first : ba::kAttnMaxBlocks;
-    // launch shape from the launch's longest key set
+    // this launch's segment tables (checked above); launch shape from its
+    // longest key set
+    ba::AttnBlock tables[ba::kAttnMaxBlocks];
     int64_t max_keys = 0;
-    for (int i = 0; i < nb; ++i) max_keys = block_keys[first + i] > max_keys ? block_keys[first + i] : max_keys;
+    for (int i = 0; i < nb; ++i) {
+      int64_t keys = 0;
+      block_table(meta[first + i], first + i, q_stride, cache, text, &tables[i], &keys);
+      if (keys > max_keys) max_keys = keys;
+    }
     const int shape = bf16 ? ba::attention_bf16_shape(D, max_keys) : 0;
     const int qtile = bf16 ? ba::attention_bf16_q_tile(D, shape) : ba::attention_f32_q_tile();
     int resident = 0;   // workgroups the device holds at once (split schedule)
@@ -362,7 +387,7 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
     int64_t tasks = 0, work = 0;
     for (int i = 0; i < nb; ++i) {
       ba::AttnBlock& B = a.blk[i];
-      B = blocks[first + i];
+      B = tables[i];
       if (B.q_len > qm) qm = B.q_len;
       B.nqt = (B.q_len + qtile - 1) / qtile;
       for (int sg = 0; sg < B.n_segs; ++sg) B.n_tiles += (B.len[sg] + ba::kKeyTile - 1) / ba::kKeyTile;

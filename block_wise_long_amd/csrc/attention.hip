@@ -21,13 +21,19 @@
 //     MFMA exactly as given; the scale c = scale*log2(e) and the reference
 //     maximum are applied to the fp32 scores by one FMA each, so the score
 //     error does not grow with the score's magnitude.
-//   * The running maximum is lazy: scores are taken relative to a reference m
-//     that is raised only when a group's weights would exceed 2^12 (checked on
-//     the group's weight sum, which bounds its largest weight), so the common
-//     path spends one FMA and one v_exp_f32 per score and no max at all.  The
-//     result is exact softmax: out = (sum p v) / (sum p) with a common m.
+//   * Scores are taken relative to a reference maximum m, the chunk's first
+//     group's maximum.  Head dim 64 (fast form) never moves it and takes the
+//     weight sums on the matrix cores (a 16x16x32 product per 16 keys with a
+//     0/1 selector operand), so the vector ALUs spend one FMA, one
+//     v_exp_f32 and half a bf16 conversion per score and nothing else; a
+//     chunk whose weights overflow is computed again with a per-group check
+//     that raises m by whole numbers (exact form).  Head dim 128 sums the
+//     weights in fp32 on the vector ALUs and raises m whenever a group's
+//     weight sum exceeds 2^12.  Either way the result is exact softmax:
+//     out = (sum p v) / (sum p) with a common m.
 //   * The weights are rounded to bf16 for the PV product; the row sums are
-//     taken in fp32 from the unrounded exponentials.
+//     taken from the rounded weights (head dim 64) or in fp32 from the
+//     unrounded exponentials (head dim 128).
 //   * K and V^T tiles of 64 keys rotate through three LDS buffers with an XOR
 //     swizzle of 16-byte chunks (conflict-free ds_read_b128 for the MFMA
 //     operands).  The tile after next streams from global memory straight
@@ -51,10 +57,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKTile = kKeyTile;   // keys per LDS tile
-constexpr float kLazyThreshold = 4096.0f;   // 2^12: bound on a group's weight sum
+constexpr float kLazyLog2 = 12.0f;          // scaled scores above m + 12 (weights above 2^12) raise m
+constexpr float kLazyThreshold = 4096.0f;   // 2^12: the same bound on a group's weight sum
 constexpr float kLn2 = 0.693147180559945309f;
 
 
@@ -118,6 +126,7 @@ struct WaveState {
   f32x16 o[D / 32];    // O^T accumulator: lane owns query lane%32, 16 dims per block
   float m_ref;         // reference maximum (exp2 domain); equal in lanes l, l^32
   float l_sum;         // this lane's share of the weight sum
+  f32x4 l_acc;         // fast path: weight sums on the matrix cores (see row_sums)
 };
 
 // Launch shapes: waves per workgroup (32 queries each).  S = 0, the wide
@@ -140,6 +149,8 @@ template <int D> constexpr int kLdsAhead = 3;
 // the step's last MFMA, so that one wave's MFMA phase overlaps the other's
 // VALU phase (measured 4 % faster at the 720p block; the same at D = 64).
 template <int D> constexpr bool kSplitPhases = D == 128;
+// Weight sums on the matrix cores (see pipe_step): head dim 64 only.
+template <int D> constexpr bool kMatrixSums = D == 64;
 
 // Tile<D, S>: the LDS layout (the same for every shape) and the launch shape
 template <int D, int S = 0>
@@ -162,6 +173,11 @@ struct Tile {
   // a round's lanes keep the chunk (column) and row-order offsets of the first
   // round: both swizzles and the row order repeat every 16 rows
   static_assert(K_ROWS_STEP % 16 == 0 && V_DIMS_STEP % 16 == 0, "copy round strides");
+  // a V lane's chunk sits in V^T rows below VW * 8 and columns below 64 of
+  // its tile: its 32-bit byte offset stays below 2 * VW * 8 * T_pad, in range
+  // for every slot stride the host accepts
+  static_assert(VW * 8 <= 32 && (unsigned long long)2 * 32 * kAttnMaxSlotStride <= (1ull << 32),
+                "32-bit copy offsets");
 
   // XOR swizzle of the 16-byte chunks of a row.  A b128 LDS access is served
   // 8 lanes per 128 bytes or 16 lanes per 256 bytes of banks; consecutive
@@ -287,18 +303,51 @@ __device__ __forceinline__ void accumulate(const u32x4* L, int lane, int g, cons
     }
 }
 
-// Adds a pair of weights to the running sums la, lb (two chains, so that
-// consecutive additions do not wait for each other).  The sums are taken in
-// fp32 from the unrounded exponentials, as the row sums of FlashAttention
-// are; the PV product uses the weights rounded to bf16.  (v_dot2_f32_bf16 on
-// the rounded pair costs more than the two additions on gfx950.)
-__device__ __forceinline__ void add_pair(float e0, float e1, float& la, float& lb) {
-  la += e0;
-  lb += e1;
+// Weight sums on the matrix cores (fast path).  v_mfma_f32_16x16x32_bf16
+// reads its B operand as 32 (k) x 16 (n): lane l gives column l % 16, rows
+// 8 (l / 16) .. + 7.  Handed the weights of one 16-key k-step in their PV
+// layout (lane l: query l % 32, keys 8 (l / 32) .. + 7), lane groups 0 and 2
+// hold queries 0-15 and groups 1 and 3 queries 16-31.  With A row 0 = 1 over
+// k-groups 0 and 2 and row 1 = 1 over groups 1 and 3 (all else 0), output row 0
+// is the k-step's weight sum of queries 0-15 and row 1 that of queries 16-31,
+// in register 0 and 1 of lanes 0-15.  The sums are of the bf16 weights the PV
+// product multiplies.  The A operand: ones in lanes 0 and 32 (row 0) and 17
+// and 49 (row 1).
+__device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
+  const bool one = lane == 0 || lane == 32 || lane == 17 || lane == 49;
+  const unsigned u = one ? 0x3F803F80u : 0u;   // two bf16 1.0
+  const u32x4 v = {u, u, u, u};
+  return as_bf16x8(v);
 }
 
-// Weights of one group from its shifted scores: bf16 exp2 values packed as
-// the B operand of the PV product, and their sum.
+// The weight sum of query lane % 32 from the row-sum accumulator, in lanes
+// 0-31 (lanes 32-63 get 0, so that l_sum + its other half is the total).
+__device__ __forceinline__ float row_sum_of_lane(const f32x4& acc, int lane) {
+  const int q = lane & 31;
+  const float lo = __shfl(acc[0], q & 15);
+  const float hi = __shfl(acc[1], q & 15);
+  return lane < 32 ? (q < 16 ? lo : hi) : 0.f;
+}
+
+// Scaled scores of one group relative to the reference maximum m:
+// score * c - m, one FMA each; keys at or past the group's `valid` count
+// (>= 32: all valid) get -inf in a fix-up that only tail groups run.
+__device__ __forceinline__ void scale_scores(const f32x16& s_in, float c, float m, int valid, f32x16& sc) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(s_in[i], c, -m);
+  if (__builtin_expect(valid < 32, 0)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // key of element i: 16(i/8) + i%8 in lanes 0-31, 8 more in lanes 32-63
+      const int key = 16 * (i >> 3) + (i & 7);
+      const uint64_t keep = (key < valid ? 0xFFFFFFFFull : 0ull) | (key + 8 < valid ? ~0xFFFFFFFFull : 0ull);
+      sc[i] = mask_inplace(sc[i], keep);
+    }
+  }
+}
+
+// Weights of one group from its scaled scores, shifted by `shift`: bf16
+// exp2 values packed as the B operand of the PV product, and their fp32 sum.
 __device__ __forceinline__ float weights(const f32x16& s, float shift, bf16x8 (&p)[2]) {
   float la = 0.f, lb = 0.f;
 #pragma unroll
@@ -312,49 +361,90 @@ __device__ __forceinline__ float weights(const f32x16& s, float shift, bf16x8 (&
       pr[1] = (__bf16)e1;
       p[k2][i] = pr[0];
       p[k2][i + 1] = pr[1];
-      add_pair(e0, e1, la, lb);
+      la += e0;
+      lb += e1;
     }
   return la + lb;
 }
 
-// One pipeline step for group k: the matrix cores take S^T of group k+1 and
-// O^T += V^T P^T of group k-1 while the vector ALUs turn the raw scores of
-// group k into weights.  P of group k replaces p on exit.  `valid` counts the
-// group's keys that lie before its segment's end (>= 32: all); the others get
-// score -inf in a fix-up that only tail groups run, ahead of the hot block.
+// One pipeline step for group k: the matrix cores take S^T of group k+1,
+// O^T += V^T P^T of group k-1 and that group's weight sums (two 16x16x32
+// products, see row_sum_selector) while the vector ALUs turn the raw scores
+// of group k into weights.  P of group k replaces p on exit.  `valid` counts
+// the group's keys that lie before its segment's end (see scale_scores).
+//
+// The scores are taken relative to a reference maximum m that starts as the
+// chunk's first group's maximum (first_reference).  The fast form never
+// moves m: the vector ALUs spend one FMA, one exponential and half a bf16
+// conversion per score, nothing else.  A chunk whose weights overflow is
+// detected at its end and computed again with `exact` set: then each group
+// first checks for a scaled score more than 12 above m (a weight above
+// 2^12; one v_max3 per three scores), and the rare raise moves m by a whole
+// number, so that O, the row sums and the pending weights of group k-1 scale
+// by an exact power of two, and the group's scores are scaled again.
+//
+// Head dim 128 has twice the matrix work per score and is bound by the
+// matrix cores: there the sums are fp32 additions of the unrounded weights
+// on the vector ALUs instead (kMatrixSums), the one form checks every group
+// (its weight sum, which bounds its largest weight, against 2^12) after the
+// MFMAs, and a raise multiplies O and the sum by exp2(-raise) and recomputes
+// the group's weights.
 template <int D>
 __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* Lp, int gp, int lane,
                                           const bf16x8 (&qf)[D / 16], float c, const f32x16& s_in,
-                                          f32x16& s_out, bf16x8 (&p)[2], int valid, bool first,
-                                          WaveState<D>& w) {
+                                          f32x16& s_out, bf16x8 (&p)[2], int valid, bool exact,
+                                          const bf16x8& sel, WaveState<D>& w) {
   constexpr int NOB = D / 32;
+  constexpr bool MS = kMatrixSums<D>;
   f32x16 sc;
-  const float mneg = -w.m_ref;
+  scale_scores(s_in, c, w.m_ref, valid, sc);
+  if (MS && __builtin_expect(exact, 0)) {
+    // Does any scaled score exceed 12?  Compared as integers (v_max3_i32, no
+    // NaN handling): a float above 12 has a larger bit pattern than 12, a
+    // negative one (and -inf) a negative pattern.
+    int mb[5];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) sc[i] = __builtin_fmaf(s_in[i], c, mneg);
-  if (__builtin_expect(valid < 32, 0)) {
+    for (int j = 0; j < 5; ++j)
+      mb[j] = max(max(__float_as_int(sc[3 * j]), __float_as_int(sc[3 * j + 1])), __float_as_int(sc[3 * j + 2]));
+    const int mbits = max(max(max(mb[0], mb[1]), mb[2]), max(max(mb[3], mb[4]), __float_as_int(sc[15])));
+    if (__any(mbits > __float_as_int(kLazyLog2))) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      // key of element i: 16(i/8) + i%8 in lanes 0-31, 8 more in lanes 32-63
-      const int key = 16 * (i >> 3) + (i & 7);
-      const uint64_t keep = (key < valid ? 0xFFFFFFFFull : 0ull) | (key + 8 < valid ? ~0xFFFFFFFFull : 0ull);
-      sc[i] = mask_inplace(sc[i], keep);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+      mx = fmaxf(mx, exchange_half(mx));
+      const int delta = mx > 0.f ? (int)ceilf(mx) : 0;
+      const float alpha = ldexpf(1.0f, -delta);
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.o[ob][i] *= alpha;
+      // lanes 0-15 hold the sums of queries lane (register 0) and lane + 16 (1)
+      const float alpha_hi = __shfl(alpha, (lane & 15) + 16);
+      w.l_acc[0] *= alpha;
+      w.l_acc[1] *= alpha_hi;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[k2][i] = (__bf16)((float)p[k2][i] * alpha);
+      w.m_ref += (float)delta;
+      scale_scores(s_in, c, w.m_ref, valid, sc);
     }
   }
   // ---- hot block: matrix cores and vector ALUs work side by side ----------
   // The wave issues in order, so the step is laid out by hand: each MFMA is
   // followed by the LDS read of the operand three MFMAs ahead and, at D = 64,
-  // by its share of the weight computation (one of eight chunks); at
-  // D = 128 the chunks all follow the last MFMA (kSplitPhases).  Scheduling
-  // barriers keep the compiler from regrouping them.
-  float l_g;
+  // by its share of the weight computation (one of eight chunks: two
+  // exponentials and their bf16 pair); at D = 128 the chunks all follow the
+  // last MFMA (kSplitPhases).  The two row-sum products follow the first and
+  // the next-to-last MFMA.  Scheduling barriers keep the compiler from
+  // regrouping them.
   {
     // nothing of the LGKM counter is outstanding here: with that known, each
     // MFMA below waits only for its own operand
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     using T = Tile<D>;
     constexpr int NKS = D / 16;
-    constexpr int NM = NKS + 2 * NOB;           // MFMAs of the step
+    constexpr int NM = NKS + 2 * NOB;           // MFMAs of the step reading LDS operands
     constexpr int LA = kLdsAhead<D>;            // LDS reads in flight ahead of use
     const int half = lane >> 5;
     const int r = 32 * gs + (lane & 31);
@@ -384,6 +474,10 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
         w.o[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], p[k2], w.o[ob], 0, 0, 0);
       }
       if (m + LA < NM) fr[m + LA] = operand(m + LA);
+      if constexpr (MS) {
+        if (m == 0) w.l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p[0], w.l_acc, 0, 0, 0);
+        if (m == NM - 2) w.l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p[1], w.l_acc, 0, 0, 0);
+      }
       if (kSplitPhases<D> && m == NM - 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (; chunk < 8 && (kSplitPhases<D> ? m == NM - 1 : chunk * NM < 8 * (m + 1)); ++chunk) {
@@ -395,37 +489,55 @@ __device__ __forceinline__ void pipe_step(const u32x4* Ls, int gs, const u32x4* 
         pr[1] = (__bf16)e1;
         pn[k2][i] = pr[0];
         pn[k2][i + 1] = pr[1];
-        if (chunk == 0) {        // the first pair starts the two chains (0 + x is not folded: -0)
-          la = e0;
-          lb = e1;
-        } else {
-          add_pair(e0, e1, la, lb);
+        if constexpr (!MS) {
+          if (chunk == 0) {        // the first pair starts the two chains (0 + x is not folded: -0)
+            la = e0;
+            lb = e1;
+          } else {
+            la += e0;
+            lb += e1;
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_g = la + lb;
     s_out = s;
     p[0] = pn[0];
     p[1] = pn[1];
+    if constexpr (!MS) {
+      float l_g = la + lb;
+      // the group's weight sum bounds each weight: raise the reference when large
+      if (__builtin_expect(__any(l_g > kLazyThreshold), 0)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+        mx = fmaxf(mx, exchange_half(mx));
+        const float delta = fmaxf(mx, 0.f);
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        w.l_sum *= alpha;
+#pragma unroll
+        for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) w.o[ob][i] *= alpha;
+        w.m_ref += delta;
+        l_g = weights(sc, delta, p);
+      }
+      w.l_sum += l_g;
+    }
   }
-  // the group's weight sum bounds each weight: raise the reference when large
-  if (__builtin_expect(__any(first || l_g > kLazyThreshold), 0)) {
-    float mx = -INFINITY;
+}
+
+// The reference maximum of a chunk: the largest scaled score of its first
+// group among the valid keys (`valid` as in pipe_step), in both lanes of a
+// query.  Its weight is exp2(0) = 1, so no sum underflows.
+__device__ __forceinline__ float first_reference(const f32x16& s, float c, int valid) {
+  float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-    mx = fmaxf(mx, exchange_half(mx));
-    const float delta = first ? mx : fmaxf(mx, 0.f);
-    const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);   // O, l are 0 at first
-    w.l_sum *= alpha;
-#pragma unroll
-    for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) w.o[ob][i] *= alpha;
-    w.m_ref += delta;
-    l_g = weights(sc, delta, p);
+  for (int i = 0; i < 16; ++i) {
+    const int key = 16 * (i >> 3) + (i & 7) + 8 * (int)(__lane_id() >> 5);
+    mx = key < valid ? fmaxf(mx, s[i] * c) : mx;
   }
-  w.l_sum += l_g;
+  return fmaxf(mx, exchange_half(mx));
 }
 
 // Work unit = one 64-key tile of one task (block, head, query tile).
@@ -565,7 +677,10 @@ void attention_bf16_kernel(const AttnArgs a) {
     }
   }
 
+  const bf16x8 sel = row_sum_selector(lane);
+  __shared__ int redo_vote;                   // a fast pass overflowed in some wave
   while (pos < end) {
+    if (tid == 0) redo_vote = 0;
     // ---- the chunk: tiles [tile0, tile0 + n_tiles) of one task ----------
     const Where at = locate(a, pos);
     const AttnBlock& B = a.blk[at.b];
@@ -593,97 +708,137 @@ void attention_bf16_kernel(const AttnArgs a) {
         qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * half));
     }
 
-    // cursor at tile0: skip whole segments, then the tiles before it
-    Cursor lc;
-    {
-      int rem = tile0;
-      int sg = 0;
-      for (; sg + 1 < B.n_segs; ++sg) {
-        const int nt = (B.len[sg] + kKTile - 1) / kKTile;
-        if (rem < nt) break;
-        rem -= nt;
-      }
-      lc.seg = sg;
-      open_segment<D>(a, B, h, lc);
-      lc.off = rem * kKTile;
-    }
-    Cursor cc = lc;                           // cursor of the tile being consumed
-    load_tile<D, S>(lc, cl, wave_u, lds_addr);
-    if (n_tiles > 1) {
-      advance<D>(a, B, h, lc);
-      load_tile<D, S>(lc, cl, wave_u, lds_addr + 16u * T::CH);
-    }
-    {
-      // buffer 2 starts as zeros: the first step's deferred PV reads it
-      const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < T::LOADS; ++u)
-        if (T::CH % T::THREADS == 0 || u * T::THREADS + tid < T::CH) lds[2][u * T::THREADS + tid] = z;
-    }
-    WaveState<D> w;
-#pragma unroll
-    for (int j = 0; j < NOB; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) w.o[j][i] = 0.f;
-    w.m_ref = 0.f;
-    w.l_sum = 0.f;
-    wait_loads();
-    __syncthreads();
-
-    // Software pipeline over 32-key groups (two per tile).  Tile t lives in
-    // buffer t % 3; tile t+2 starts loading when tile t+1 is published, after
-    // every wave has issued its last read of the buffer it overwrites.  Every
-    // step has the same shape: the first step's deferred PV multiplies zero
-    // weights with the zero-filled third buffer, and the last step's look-ahead
-    // QK^T reads whatever the next buffer holds and is discarded.
-    f32x16 sa, sb;                            // raw scores of even / odd groups
-    bf16x8 p[2];                              // weights of the previous group
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[k2][i] = (__bf16)0.0f;
-    if (active) sa = scores<D>(lds[0], lane, 0, qf);
-    // one tile; its buffer index is a compile-time constant so that every LDS
-    // address of the steps is a per-lane base plus an immediate offset
-    auto tile = [&](auto buf_c, int t) {
-      constexpr int buf = decltype(buf_c)::value;
-      constexpr int nbuf = buf == 2 ? 0 : buf + 1;
-      constexpr int pbuf = buf == 0 ? 2 : buf - 1;
-      const int valid = cc.len - cc.off;
-      // group 2t: S of group 2t+1 (same tile), PV of group 2t-1 (previous tile)
-      if (active)
-        pipe_step<D>(lds[buf], 1, lds[pbuf], 1, lane, qf, c, sa, sb, p, valid, t == 0, w);
-      if (t + 1 < n_tiles) {
-        // publish tile t+1, start loading tile t+2 into the buffer of tile t-1
-        wait_loads();
-        __syncthreads();
-        if (t + 2 < n_tiles) {
-          advance<D>(a, B, h, lc);
-          load_tile<D, S>(lc, cl, wave_u, lds_addr + 16u * T::CH * pbuf);
+    // The chunk's pass over its key tiles, in the fast form first and, if a
+    // wave of the workgroup overflowed, again in the exact one (see
+    // pipe_step): the same loop, with a wave-uniform flag.
+    for (int exact = 0; exact < 2; ++exact) {
+      // cursor at tile0: skip whole segments, then the tiles before it
+      Cursor lc;
+      {
+        int rem = tile0;
+        int sg = 0;
+        for (; sg + 1 < B.n_segs; ++sg) {
+          const int nt = (B.len[sg] + kKTile - 1) / kKTile;
+          if (rem < nt) break;
+          rem -= nt;
         }
-        advance<D>(a, B, h, cc);
+        lc.seg = sg;
+        open_segment<D>(a, B, h, lc);
+        lc.off = rem * kKTile;
       }
-      // group 2t+1: S of group 2t+2 (next tile), PV of group 2t (this tile)
-      if (active)
-        pipe_step<D>(lds[nbuf], 0, lds[buf], 0, lane, qf, c, sb, sa, p, valid - 32, false, w);
-    };
-    for (int t = 0; t < n_tiles;) {
-      tile(std::integral_constant<int, 0>{}, t);
-      if (++t >= n_tiles) break;
-      tile(std::integral_constant<int, 1>{}, t);
-      if (++t >= n_tiles) break;
-      tile(std::integral_constant<int, 2>{}, t);
-      ++t;
-    }
-    // the last group's PV (group 1 of the last tile)
-    if (active) accumulate<D>(lds[(n_tiles - 1) % 3], lane, 1, p, w.o);
+      Cursor cc = lc;                           // cursor of the tile being consumed
+      load_tile<D, S>(lc, cl, wave_u, lds_addr);
+      if (n_tiles > 1) {
+        advance<D>(a, B, h, lc);
+        load_tile<D, S>(lc, cl, wave_u, lds_addr + 16u * T::CH);
+      }
+      {
+        // buffer 2 starts as zeros: the first step's deferred PV reads it
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < T::LOADS; ++u)
+          if (T::CH % T::THREADS == 0 || u * T::THREADS + tid < T::CH) lds[2][u * T::THREADS + tid] = z;
+      }
+      WaveState<D> w;
+#pragma unroll
+      for (int j = 0; j < NOB; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.o[j][i] = 0.f;
+      w.m_ref = 0.f;
+      w.l_sum = 0.f;
+      w.l_acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      wait_loads();
+      __syncthreads();
 
-    if (whole) {
-      store_output<D>(a, b, h, qrow, row_ok, half, w);
-    } else {
-      // a cut task: the merge kernel combines the pieces after this launch
-      store_partial<D, S>(a.partials + ((int64_t)2 * (x * a.tail_wg + tail_j) + (first_chunk ? 0 : 1)) *
-                                        Partial<D, S>::FLOATS, wave, lane, w);
+      // Software pipeline over 32-key groups (two per tile).  Tile t lives in
+      // buffer t % 3; tile t+2 starts loading when tile t+1 is published, after
+      // every wave has issued its last read of the buffer it overwrites.  Every
+      // step has the same shape: the first step's deferred PV multiplies zero
+      // weights with the zero-filled third buffer, and the last step's look-ahead
+      // QK^T reads whatever the next buffer holds and is discarded.
+      f32x16 sa, sb;                            // raw scores of even / odd groups
+      bf16x8 p[2];                              // weights of the previous group
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[k2][i] = (__bf16)0.0f;
+      if (active) {
+        sa = scores<D>(lds[0], lane, 0, qf);
+        w.m_ref = first_reference(sa, c, cc.len - cc.off);
+      }
+      // one tile; its buffer index is a compile-time constant so that every LDS
+      // address of the steps is a per-lane base plus an immediate offset
+      auto tile = [&](auto buf_c, int t) {
+        constexpr int buf = decltype(buf_c)::value;
+        constexpr int nbuf = buf == 2 ? 0 : buf + 1;
+        constexpr int pbuf = buf == 0 ? 2 : buf - 1;
+        const int valid = cc.len - cc.off;
+        // group 2t: S of group 2t+1 (same tile), PV of group 2t-1 (previous tile)
+        if (active)
+          pipe_step<D>(lds[buf], 1, lds[pbuf], 1, lane, qf, c, sa, sb, p, valid, exact != 0, sel, w);
+        if (t + 1 < n_tiles) {
+          // publish tile t+1, start loading tile t+2 into the buffer of tile t-1
+          wait_loads();
+          __syncthreads();
+          if (t + 2 < n_tiles) {
+            advance<D>(a, B, h, lc);
+            load_tile<D, S>(lc, cl, wave_u, lds_addr + 16u * T::CH * pbuf);
+          }
+          advance<D>(a, B, h, cc);
+        }
+        // group 2t+1: S of group 2t+2 (next tile), PV of group 2t (this tile)
+        if (active)
+          pipe_step<D>(lds[nbuf], 0, lds[buf], 0, lane, qf, c, sb, sa, p, valid - 32, exact != 0, sel, w);
+      };
+      // Tile t lives in buffer t % 3.  Whole rounds of three tiles, then the
+      // remainder: a loop with one exit (with an exit after each tile the
+      // compiler kept the accumulators in different registers in each copy
+      // and spilled them).
+      int t = 0;
+      for (; t + 3 <= n_tiles; t += 3) {
+        tile(std::integral_constant<int, 0>{}, t);
+        tile(std::integral_constant<int, 1>{}, t + 1);
+        tile(std::integral_constant<int, 2>{}, t + 2);
+      }
+      if (t < n_tiles) tile(std::integral_constant<int, 0>{}, t++);
+      if (t < n_tiles) tile(std::integral_constant<int, 1>{}, t++);
+      // the last group's PV (group 1 of the last tile)
+      if (active) {
+        accumulate<D>(lds[(n_tiles - 1) % 3], lane, 1, p, w.o);
+        if constexpr (kMatrixSums<D>) {
+          w.l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p[0], w.l_acc, 0, 0, 0);
+          w.l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p[1], w.l_acc, 0, 0, 0);
+        }
+      }
+      // the weight sums from the matrix cores
+      if constexpr (kMatrixSums<D>) w.l_sum = row_sum_of_lane(w.l_acc, lane);
+      if (kMatrixSums<D> && !exact) {
+        // A fast pass overflowed where a sum or an accumulator is not
+        // finite, or a sum is past 2^100 (beyond it the accumulators may
+        // overflow for large values): then the whole workgroup computes the
+        // chunk again in the exact form.
+        float chk = w.l_sum;
+#pragma unroll
+        for (int j = 0; j < NOB; ++j)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) chk += w.o[j][i];
+        const bool bad = active && !(__builtin_isfinite(chk) && w.l_sum < 0x1p100f);
+        // the flag was cleared before this pass's first barrier and is cleared
+        // again only after the chunk's closing barrier, when every wave has
+        // read it; this barrier also orders every wave's last LDS read before
+        // the copies of a second pass
+        if (bad) redo_vote = 1;
+        __syncthreads();
+        if (redo_vote != 0) continue;
+      }
+      if (whole) {
+        store_output<D>(a, b, h, qrow, row_ok, half, w);
+      } else {
+        // a cut task: the merge kernel combines the pieces after this launch
+        store_partial<D, S>(a.partials + ((int64_t)2 * (x * a.tail_wg + tail_j) + (first_chunk ? 0 : 1)) *
+                                          Partial<D, S>::FLOATS, wave, lane, w);
+      }
+      break;
     }
     pos += n_tiles;
     first_chunk = false;

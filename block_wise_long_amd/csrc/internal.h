@@ -13,6 +13,10 @@ constexpr int kAppendMaxBlocks = 64;     // slots per append launch (kernarg)
 constexpr int kAttnMaxBlocks = 16;       // blocks per attention launch (kernarg)
 constexpr int kAttnMaxSegs = 9;          // 8 cache segments + text
 constexpr int kUpdateMaxBlocks = 64;     // blocks per update launch (kernarg)
+// The bf16 attention kernel addresses a lane's V^T chunk of a ring matrix by
+// a 32-bit byte offset below (32 * T_pad) * 2 from the segment's base: ring
+// slot strides (T_pad) of bf16 rings it reads stay below this.
+constexpr int64_t kAttnMaxSlotStride = (int64_t)1 << 26;
 
 // ---- ring append -----------------------------------------------------------
 struct AppendArgs {

@@ -142,7 +142,14 @@ typedef struct {
  * q, out:  [n_blocks][q_stride][heads][head_dim], the ring's dtype.  Rows
  *          i >= q_len of a block are neither read nor written.  out may be q.
  * cache:   the K/V ring; text: a ring with the text K/V (same heads,
- *          head_dim, dtype), or NULL when every text_len is 0.
+ *          head_dim, dtype), or NULL when every text_len is 0.  The text
+ *          K/V is passed as a ring (appended once per prompt with
+ *          ba_cache_append; meta[b].text_slot picks the slot) rather than as
+ *          plain [heads][text_len][head_dim] arrays: a ring matrix stores V
+ *          transposed ([head_dim][T_pad] per head), which is the layout the
+ *          PV product streams from, so the text keys take the same path
+ *          through the kernel as the cached segments, with no per-call
+ *          transpose.
  * meta:    (host) n_blocks entries.  Every block with q_len > 0 needs >= 1 key.
  * scale:   > 0, or <= 0 for 1/sqrt(head_dim).
  * lse:     optional [n_blocks][heads][q_stride] fp32 log-sum-exp (natural
@@ -161,9 +168,11 @@ typedef struct {
  *          Results agree to rounding either way and are deterministic.  Its
  *          contents need no initialisation; calls that share a workspace must
  *          be ordered on one stream.
- * bf16: products of bf16 inputs accumulate in fp32; the normalised weights
- * are rounded to bf16 for the second product and the output to bf16 (nearest
- * even).  fp32: all arithmetic in fp32 (the workspace is not used).
+ * bf16: products of bf16 inputs accumulate in fp32; the weights are rounded
+ * to bf16 (nearest even) for the second product and the output to bf16.
+ * The weight sums are taken in fp32 of the rounded weights at head_dim 64
+ * (on the matrix cores) and of the unrounded ones at head_dim 128.
+ * fp32: all arithmetic in fp32 (the workspace is not used).
  */
 ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cache,
                              const ba_ring* text, const ba_block_meta* meta,

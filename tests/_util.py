@@ -66,13 +66,40 @@ def check_contract(got, ref, dtype, gate2=True):
 
 
 def sample_rows(q_len, n_random=48, seed=0, tile=128):
-    """Edge rows (first, tile boundaries, ragged tail, last) plus random rows."""
+    """Edge rows plus random rows.  tile is the launch's query tile
+    (ba_attention_query_tile): every tile boundary, and in the first and the
+    last tile every 32-query wave boundary; the ragged tail; random rows."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    rows = {0, 1, 31, 32, 63, 64, tile - 1, tile, q_len - 1, q_len - 2}
+    rows = {0, 1, q_len - 1, q_len - 2}
+    for t0 in range(0, q_len, tile):
+        rows |= {t0 - 1, t0, t0 + 1}
     last_tile = (q_len - 1) // tile * tile
-    rows |= {last_tile, last_tile + 1}
+    for t0 in (0, last_tile):
+        for w0 in range(t0, t0 + tile, 32):
+            rows |= {w0 - 1, w0, w0 + 31}
     rows |= set(rng.integers(0, q_len, n_random).tolist())
     return sorted(r for r in rows if 0 <= r < q_len)
+
+
+def cut_heads(n_blocks, heads, q_len, tile, tail_wg):
+    """Heads of the tasks that the split schedule cuts into pieces, given the
+    tail workgroups per XCD that ba_attention_plan reports (0: none cut).
+    Tasks are (block, head, query tile), head-major within a block; XCD x owns
+    tasks [x n / 8, (x + 1) n / 8); its last round, or the last two when the
+    last is under a quarter full, is shared by the tail workgroups."""
+    if tail_wg <= 0:
+        return []
+    nqt = -(-q_len // tile)
+    n = n_blocks * heads * nqt
+    cut = set()
+    for x in range(8):
+        t0, t1 = x * n // 8, (x + 1) * n // 8
+        rounds = (t1 - t0) // tail_wg
+        if ((t1 - t0) - rounds * tail_wg) * 4 < tail_wg and rounds > 0:
+            rounds -= 1
+        for t in range(t0 + rounds * tail_wg, t1):
+            cut.add((t % (heads * nqt)) // nqt)
+    return sorted(cut)
 
 
 class Workload:

@@ -196,6 +196,27 @@ def test_attention_plan_on_the_host():
     assert plan(c, None, [_meta()], out=None) == B.BA_ERR_INVALID_ARG
 
 
+def test_attention_rejects_ring_strides_past_32bit_copy_offsets():
+    # the bf16 kernel addresses a lane's V^T chunk by a 32-bit byte offset
+    # below 2 * 32 * slot stride: strides from 2^26 tokens on are refused
+    # before anything is planned or launched; the fp32 kernel has no such limit
+    tail = ctypes.c_int32(-1)
+
+    def plan(cache, text, metas):
+        arr = (B.ba_block_meta * len(metas))(*metas)
+        return B.raw.ba_attention_plan(16, ctypes.byref(cache), ctypes.byref(text) if text is not None else None,
+                                       arr, len(metas), 0, ctypes.byref(tail))
+    lim = 1 << 26
+    assert plan(_ring(slot_tokens=lim - 64), None, [_meta()]) == B.BA_OK
+    assert plan(_ring(slot_tokens=lim - 63), None, [_meta()]) == B.BA_ERR_OUT_OF_RANGE
+    assert "stride" in B.ba_last_error()
+    assert plan(_ring(slot_tokens=lim), None, [_meta()]) == B.BA_ERR_OUT_OF_RANGE
+    assert plan(_ring(), _ring(1, lim - 63), [_meta(text_len=3)]) == B.BA_ERR_OUT_OF_RANGE
+    assert plan(_ring(), _ring(1, lim - 64), [_meta(text_len=3)]) == B.BA_OK
+    assert plan(_ring(slot_tokens=lim, dtype=B.BA_F32), None, [_meta()]) == B.BA_OK
+    assert _attn(_ring(slot_tokens=lim), None, [_meta()]) == B.BA_ERR_OUT_OF_RANGE
+
+
 def test_workspace_bytes_without_device():
     # fp32 never uses one; with no device to size the grid, none is asked for
     # query tiles: whole waves of 32 queries (bf16), 64 (fp32); 0 when unsupported

@@ -246,6 +246,38 @@ def test_growing_scores_with_ragged_segments_and_text(D):
     assert np.nanmax(np.abs(lse.cpu().numpy() - ref_lse) / np.maximum(1, np.abs(ref_lse))) < 1e-3
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("growth", [6.0, 40.0, 90.0, 300.0])
+def test_scores_rising_along_the_keys(D, growth):
+    # scores rise linearly along the key sequence by `growth` (exp2 domain)
+    # above the first group's maximum.  Head dim 64's fast form keeps its
+    # first reference: at 6 the weights stay within [0, 2^6], at 40 and 90
+    # they grow to 2^40 and 2^90 (sums near 2^94, below the 2^100 check); at
+    # 300 they overflow fp32 and the chunk is computed again in the exact
+    # form.  Head dim 128 raises its reference whenever a group's weights
+    # pass 2^12.  Every case matches the oracle.
+    rng = _rng(15 + D + int(growth))
+    H, L = 2, 700
+    w = Workload("bf16", 1, L, H, D, 0)
+    k = np.zeros((L, H, D))
+    k[:, :, 0] = (growth / math.log2(math.e)) * np.arange(L)[:, None] / L
+    k[:, :, 1] = N.bf16_bits_to_f64(draw(rng, (L, H), 0.25, "bf16"))
+    w.append(N.f64_to_bf16_bits(k), draw(rng, (L, H, D), 1.0, "bf16"))
+    q = np.zeros((1, 200, H, D))
+    q[..., 0] = 1.0
+    q[..., 1] = N.bf16_bits_to_f64(draw(rng, (1, 200, H), 1.0, "bf16"))
+    qb = N.f64_to_bf16_bits(q)
+    metas = [{"q_len": 200, "segs": [(0, L)], "text_slot": 0, "text_len": 0}]
+    out, lse = w.run(qb, metas, scale=1.0)
+    ref, ref_lse = w.oracle(qb, metas, scale=1.0)
+    got = decode(out, "bf16")
+    assert not np.isnan(got).any()
+    # a few dozen keys carry the weight: each output is an average of a few
+    # values of |v| ~ 1, with the weights rounded to bf16
+    assert np.max(np.abs(got - ref)) <= 2 ** -6 * max(1.0, np.max(np.abs(ref)))
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse) / np.maximum(1, np.abs(ref_lse))) < 1e-3
+
+
 def test_in_place_output():
     import torch
     import block_wise_long_amd as B

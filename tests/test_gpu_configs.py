@@ -5,12 +5,13 @@ random rows) for every head or a spread of heads; config 0 (fp32) in full."""
 import numpy as np
 import pytest
 
-from _util import build_config, check_contract, decode, ring_bytes, sample_rows
+from _util import build_config, check_contract, cut_heads, decode, ring_bytes, sample_rows
 from workloads import CONFIGS
 
 pytestmark = pytest.mark.gpu
 
-# heads checked per config (all where the oracle stays within seconds)
+# heads checked per config (all where the oracle stays within seconds), plus
+# every head whose tasks the launch's split schedule cuts
 HEADS = {0: None, 1: None, 2: [0, 1, 13, 26, 39], 3: [0, 11, 23], 4: None}
 N_RANDOM_ROWS = {0: 0, 1: 40, 2: 24, 3: 16, 4: 64}
 
@@ -23,8 +24,22 @@ def test_config_parity(idx):
     assert ring_bytes(w.text) == w.otext.as_bytes()
     q = inputs["q"]
     out, lse = w.run(q, metas)
-    rows = None if idx == 0 else sample_rows(cfg.q_len, N_RANDOM_ROWS[idx], seed=idx)
-    ref, ref_lse = w.oracle(q, metas, heads=HEADS[idx], rows=rows)
+    B = w.B
+    heads = HEADS[idx]
+    rows = None
+    if idx != 0:
+        # edge rows of the launch's own query tile; heads of the cut tasks
+        tile = B.ba_attention_query_tile(cfg.head_dim, B.BA_BF16, cfg.key_len)
+        rows = sample_rows(cfg.q_len, N_RANDOM_ROWS[idx], seed=idx, tile=tile)
+        ws = B.ba_attention_workspace_bytes(cfg.head_dim, B.BA_BF16, cfg.n_blocks, cfg.q_len, cfg.heads)
+        tail = B.ba_attention_plan(cfg.q_len, w.ring, w.text, metas, ws)
+        cut = cut_heads(cfg.n_blocks, cfg.heads, cfg.q_len, tile, tail)
+        if idx == 3:
+            assert cut, "the 8 queued blocks take the split schedule"
+        if heads is not None:
+            heads = sorted(set(heads) | set(cut))
+        print(f"config {idx}: tile {tile}, tail workgroups {tail}, cut heads {cut}, {len(rows)} rows")
+    ref, ref_lse = w.oracle(q, metas, heads=heads, rows=rows)
     got = decode(out, cfg.dtype)
     mx, mn = check_contract(got, ref, cfg.dtype, gate2=(idx != 0))
     print(f"config {idx}: max-abs {mx:.3e} mean-abs {mn:.3e}")

@@ -90,7 +90,10 @@ def test_split_parts_at_video_shape():
     assert B.ba_attention_plan(L, w.ring, w.text, [{"q_len": L, "segs": [], "text_slot": 0,
                                                     "text_len": TXT}], ws.numel()) == 0
     assert B.ba_attention_plan(L, w.ring, w.text, joint_m, ws.numel()) > 0
-    rows = sample_rows(L, 24, seed=72)
+    # edge rows of both launch shapes: the text-only call's narrow tile and
+    # the self and joint calls' wide one
+    rows = sorted(set(sample_rows(L, 24, seed=72, tile=B.ba_attention_query_tile(D, B.BA_BF16, TXT)))
+                  | set(sample_rows(L, 0, seed=72, tile=B.ba_attention_query_tile(D, B.BA_BF16, 2 * L + TXT))))
     heads = [0, 7, 23]
     qf = N.decode(q, "bf16")
     (ref_s, ref_ls), (ref_t, ref_lt) = A.split_text_attention_ref(qf, w.oring, w.otext, joint_m,

@@ -186,7 +186,8 @@ def test_queue_at_bench_shape_sampled():
     fq = FifoQueue(to_dev(x0, "bf16"), to_dev(tk, "bf16"), to_dev(tv, "bf16"), T=T)
     otext = oring.RingModel(1, TXT, H, D, "bf16")
     otext.append(tk, tv, TXT)
-    rows = sample_rows(L, 8, seed=54)
+    import block_wise_long_amd as B
+    rows = sample_rows(L, 8, seed=54, tile=B.ba_attention_query_tile(D, B.BA_BF16, 2 * L + TXT))
     heads = [0, 11, 23]
     for g in range(2):
         pre = to_host_bits(fq.x)
