@@ -584,6 +584,8 @@ def main():
     ap.add_argument("--also", type=lambda t: [int(x) for x in t.split(",") if x], default=[1, 2],
                     help="config indices whose attention is also timed alone (comma list, empty: none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--no-sweeps", action="store_true",
+                    help="skip the append and update size sweeps (for profiler runs of the step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--queue", action="store_true",
@@ -680,8 +682,8 @@ def main():
             continue
         others[CONFIGS[i].name] = attention_alone(B, torch, CONFIGS[i], args.steps, args.warmup, args.warmup_min_s)
 
-    update_sweep = update_size_sweep(B, torch)
-    append_sweep = append_size_sweep(B, torch)
+    update_sweep = None if args.no_sweeps else update_size_sweep(B, torch)
+    append_sweep = None if args.no_sweeps else append_size_sweep(B, torch)
 
     flops = float(cfg.flops())
     tflops_step = flops / (ms_step * 1e-3) / 1e12
