@@ -72,6 +72,8 @@ _SIGS = {
     "ba_block_attention": (_I32, [_P, _I32, ctypes.POINTER(ba_ring), ctypes.POINTER(ba_ring),
                                   ctypes.POINTER(ba_block_meta), _I32, ctypes.c_float, _P, _P,
                                   _P, ctypes.c_size_t, _P]),
+    "ba_block_attention_static": (_I32, [_P, _I32, ctypes.POINTER(ba_ring), ctypes.POINTER(ba_ring),
+                                         ctypes.POINTER(ba_block_meta), _I32, ctypes.c_float, _P, _P, _P]),
     "ba_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
     "ba_attention_query_tile": (_I32, [_I32, _I32, _I32]),
     "ba_attention_plan": (_I32, [_I32, ctypes.POINTER(ba_ring), ctypes.POINTER(ba_ring),
@@ -306,6 +308,33 @@ def ba_block_attention(q, cache, text, metas, scale=0.0, out=None, lse=None, wor
                                    _dev(lse, "lse") if lse is not None else None,
                                    ws_ptr, ws_bytes, _stream()),
            "ba_block_attention")
+    return out
+
+
+def ba_block_attention_static(q, cache, text, metas, scale=0.0, out=None, lse=None):
+    """ba_block_attention without a workspace argument: the library's own
+    per-GPU device array holds the split schedule's partial results (calls
+    on one GPU must not overlap).  Same arguments and results otherwise."""
+    nb, q_stride = q.shape[0], q.shape[1]
+    if q.shape[2] != cache.desc.heads or q.shape[3] != cache.desc.head_dim:
+        raise ValueError("q shape does not match the cache ring")
+    if len(metas) != nb:
+        raise ValueError("one meta per block")
+    arr = (ba_block_meta * max(nb, 1))()
+    for i, m in enumerate(metas):
+        arr[i] = m if isinstance(m, ba_block_meta) else make_meta(
+            m["q_len"], m["segs"], m.get("text_slot", 0), m.get("text_len", 0))
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is not None and (lse.dtype != torch.float32 or lse.numel() < nb * cache.desc.heads * q_stride):
+        raise ValueError("lse must be fp32 [n_blocks][heads][q_stride]")
+    _check(_lib.ba_block_attention_static(_dev(q, "q"), q_stride, ctypes.byref(cache.desc),
+                                          ctypes.byref(text.desc) if text is not None else None,
+                                          arr, nb, float(scale), _dev(out, "out"),
+                                          _dev(lse, "lse") if lse is not None else None, _stream()),
+           "ba_block_attention_static")
     return out
 
 

@@ -3,6 +3,7 @@
 // Every check runs before anything is enqueued; on failure nothing is
 // enqueued, no descriptor changes and ba_last_error() says why.
 #include <math.h>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -492,6 +493,72 @@ ba_status ba_attention_plan(int32_t q_stride, const ba_ring* cache, const ba_rin
   if (tail_workgroups == nullptr) return fail(BA_ERR_INVALID_ARG, "tail_workgroups is NULL");
   return attention_run(nullptr, q_stride, cache, text, meta, n_blocks, 0.f, nullptr, nullptr,
                        workspace_bytes > 0, nullptr, workspace_bytes, nullptr, tail_workgroups);
+}
+
+}  // extern "C"
+
+// ---- block attention without allocation ---------------------------------------
+// The split schedule's partial results live in the library's own device array
+// (one copy per GPU: a __device__ variable exists on every device the code
+// object is loaded on).  72 MiB holds two partial results for every workgroup
+// slot of a 256-CU device at either head dim (the most is 66 MiB, head_dim
+// 128).  Every call on a GPU shares that GPU's copy.
+namespace {
+constexpr size_t kScratchBytes = (size_t)72 << 20;
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchMaxDevices];   // device address of `scratch` per device, once known
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+// The device address of the current device's `scratch`, looked up with that
+// device current on its first use and kept (the array's name in host code is
+// not a device address).
+ba_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchMaxDevices)
+    return fail(BA_ERR_UNSUPPORTED, "device %d: the library keeps scratch for devices 0-%d", dev,
+                kScratchMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(BA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+ba_status ba_block_attention_static(const void* q, int32_t q_stride, const ba_ring* cache, const ba_ring* text,
+                                    const ba_block_meta* meta, int32_t n_blocks, float scale, void* out,
+                                    float* lse, hipStream_t stream) {
+  if (q == nullptr || out == nullptr) return fail(BA_ERR_INVALID_ARG, "q or out is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(BA_ERR_INVALID_ARG, "q or out not 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(BA_ERR_INVALID_ARG, "lse not 4-byte aligned");
+  ba_status st = check_ring(cache, "cache");
+  if (st != BA_OK) return st;
+  if (cache->dtype != BA_BF16)   // the fp32 kernel uses no scratch
+    return attention_run(q, q_stride, cache, text, meta, n_blocks, scale, out, lse, false, nullptr, 0, stream,
+                         nullptr);
+  const size_t need = ba_attention_workspace_bytes(cache->head_dim, cache->dtype, n_blocks > 0 ? n_blocks : 1,
+                                                   q_stride > 0 ? q_stride : 1, cache->heads);
+  if (need > kScratchBytes)
+    return fail(BA_ERR_OUT_OF_RANGE, "this device needs %zu bytes of split-schedule scratch; the library holds %zu",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != BA_OK) return st;
+  return attention_run(q, q_stride, cache, text, meta, n_blocks, scale, out, lse, true, ws, kScratchBytes, stream,
+                       nullptr);
 }
 
 ba_status ba_schedule_coefficients(const ba_schedule* sched, const int32_t* t, int32_t n, float* c1, float* c2) {

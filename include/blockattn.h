@@ -180,6 +180,23 @@ ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cac
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/*
+ * ba_block_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results, without a workspace argument.
+ * The split schedule's partial results go to a device array the library
+ * holds itself (72 MiB on each GPU it runs on, kept until the process
+ * ends); the call allocates nothing.  Calls on one GPU share that array:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be ordered by the caller.  BA_ERR_OUT_OF_RANGE when the device would need
+ * more than 72 MiB of partial results (more workgroup slots than 256 CUs
+ * hold); fp32 rings use no scratch.
+ */
+ba_status ba_block_attention_static(const void* q, int32_t q_stride, const ba_ring* cache,
+                                    const ba_ring* text, const ba_block_meta* meta,
+                                    int32_t n_blocks, float scale, void* out, float* lse,
+                                    hipStream_t stream);
+
 /* Workspace bytes for ba_block_attention on the current device (0: none is
  * used, e.g. fp32, or no device): two partial results per workgroup the
  * device holds at once.  A smaller buffer still works, with fewer workgroups

@@ -21,7 +21,7 @@ FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dere
 
 def test_exports_every_declared_symbol():
     names = B.header_symbols()
-    assert len(names) == 21
+    assert len(names) == 22
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -175,6 +175,21 @@ def test_attention_rejects():
     assert "head_dim" in B.ba_last_error()
     assert _attn(c, None, [_meta()], ws=FAKE + 64, ws_bytes=1 << 20) == B.BA_ERR_INVALID_ARG
     assert "workspace" in B.ba_last_error()
+
+
+def test_static_attention_rejects_before_any_device_work():
+    c = _ring()
+    f = B.raw.ba_block_attention_static
+
+    def call(q=FAKE, out=FAKE, lse=None):
+        arr = (B.ba_block_meta * 1)(_meta())
+        return f(q, 16, ctypes.byref(c), None, arr, 1, 0.0, out, lse, None)
+    assert call(q=None) == B.BA_ERR_INVALID_ARG
+    assert call(out=None) == B.BA_ERR_INVALID_ARG
+    assert call(q=FAKE + 8) == B.BA_ERR_INVALID_ARG
+    assert call(lse=FAKE + 2) == B.BA_ERR_INVALID_ARG
+    arr = (B.ba_block_meta * 1)(_meta())
+    assert f(FAKE, 16, None, None, arr, 1, 0.0, FAKE, None, None) == B.BA_ERR_INVALID_ARG
 
 
 def test_attention_plan_on_the_host():
