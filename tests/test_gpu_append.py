@@ -71,3 +71,20 @@ def test_batched_append_more_slots_than_one_launch_takes():
     v = draw(rng, (nb, n, H, D), 0.5, "bf16")
     w.append_batched(k, v, slots)
     assert ring_bytes(w.ring) == w.oring.as_bytes()
+
+
+@pytest.mark.parametrize("dtype,D,H,n,slot_tokens", [
+    ("bf16", 64, 120, 1050, 1060),   # T_pad 1088: the last 128-token tile ends half past the slot
+    ("f32", 128, 64, 2000, 2000),    # T_pad 2048
+    ("bf16", 128, 40, 3333, 3400),   # ragged count, T_pad 3456 (27 tiles of 128)
+])
+def test_large_appends_take_long_tiles_bit_exact(dtype, D, H, n, slot_tokens):
+    # enough work for the 128-token tiles (at least 1024 workgroups), with
+    # ragged counts and slot strides that are not a multiple of 128
+    rng = _rng(300 + D + H)
+    w = Workload(dtype, 2, slot_tokens, H, D, 0)
+    for m in (slot_tokens, n):
+        k = draw(rng, (m, H, D), 1.0, dtype)
+        v = draw(rng, (m, H, D), 1.0, dtype)
+        w.append(k, v)
+    assert ring_bytes(w.ring) == w.oring.as_bytes()
