@@ -48,10 +48,14 @@ PROJ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "project_d64_qkv480p_traffic.
 
 
 def attention_kernel_name(B, D, max_keys):
-    """The bf16 attention kernel a launch takes: its launch shape (0 wide, 1
-    narrow) follows from the query tile the library reports for the key set."""
+    """The bf16 attention kernel a launch takes for a one-segment key set: its
+    launch shape (0 wide, 1 narrow, 2 resident) follows from the query tile
+    the library reports for the key set."""
+    tile = B.ba_attention_query_tile(D, B.BA_BF16, max_keys)
+    if tile == 32:
+        return "attention_resident_kernel<2>"
     wide = B.ba_attention_query_tile(D, B.BA_BF16, 1 << 30)
-    return f"attention_bf16_kernel<{D}, {0 if B.ba_attention_query_tile(D, B.BA_BF16, max_keys) == wide else 1}>"
+    return f"attention_bf16_kernel<{D}, {0 if tile == wide else 1}>"
 
 
 def kernel_hash(src=ATTN_SRC):
@@ -514,11 +518,12 @@ def cross_bench(args):
     """One JSON line for the separate text cross-attention at the 480p
     block's shape: 5400 queries, 24 heads x 64, a 512-token text (a padded
     prompt), no cache segments; beside it the self part alone (cache
-    [5400 | 5400], no text) and the joint call over [cache | text]."""
+    [5400 | 5400], no text), the joint call over [cache | text], and the
+    text-only call of the 8 queued blocks of a step in one launch."""
     import torch
     import block_wise_long_amd as B
     torch.cuda.set_device(0)
-    L, H, D, TXT = 5400, 24, 64, 512
+    L, H, D, TXT, NQ = 5400, 24, 64, 512, 8
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20256)
 
@@ -528,23 +533,26 @@ def cross_bench(args):
     B.ba_cache_append_batched(ring, rnd(2, L, H, D), rnd(2, L, H, D), [0, 1])
     text = B.ba_ring_init(1, TXT, H, D, B.BA_BF16)
     B.ba_cache_append(text, rnd(TXT, H, D), rnd(TXT, H, D), TXT)
-    q = rnd(1, L, H, D)
+    q = rnd(NQ, L, H, D)
     out = torch.empty_like(q)
     segs = [(0, L), (1, L)]
     m_cross = [B.make_meta(L, [], 0, TXT)]
     m_self = [B.make_meta(L, segs, 0, 0)]
     m_joint = [B.make_meta(L, segs, 0, TXT)]
+    m_queue = [B.make_meta(L, [], 0, TXT) for _ in range(NQ)]
     stream = torch.cuda.current_stream()
 
     def timed(metas):
-        for _ in range(max(args.warmup, 1)):
-            B.ba_block_attention(q, ring, text, metas, out=out)
-        torch.cuda.synchronize()
+        nb = len(metas)
+
+        def call():
+            B.ba_block_attention(q[:nb], ring, text, metas, out=out[:nb])
+        warm_up(torch, call, max(args.warmup, 1), args.warmup_min_s)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         for e0, e1 in evs:
             e0.record(stream)
-            B.ba_block_attention(q, ring, text, metas, out=out)
+            call()
             e1.record(stream)
         torch.cuda.synchronize()
         return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
@@ -552,8 +560,10 @@ def cross_bench(args):
     ms_cross = timed(m_cross)
     ms_self = timed(m_self)
     ms_joint = timed(m_joint)
+    ms_queue = timed(m_queue)
     flops = 4.0 * L * TXT * D * H
     tf = flops / (ms_cross * 1e-3) / 1e12
+    tf_q = NQ * flops / (ms_queue * 1e-3) / 1e12
     res = {"metric": "separate text cross-attention TFLOP/s at 1 GPU",
            "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_cross, 5), "higher_is_better": True, "scaling": "weak",
@@ -567,7 +577,10 @@ def cross_bench(args):
            "hbm_bytes_per_launch": 2 * L * H * D * 2 + 2 * TXT * H * D * 2,
            "self_only_ms": round(ms_self, 5),
            "split_ms": round(ms_self + ms_cross, 5),
-           "joint_ms": round(ms_joint, 5)}
+           "joint_ms": round(ms_joint, 5),
+           # the queue step's text-only call: its 8 blocks in one launch
+           "queued_8_blocks": {"ms": round(ms_queue, 5), "tflops": round(tf_q, 2),
+                               "frac": round(tf_q / PEAK_BF16_TFLOPS, 4)}}
     print(json.dumps(res), flush=True)
 
 

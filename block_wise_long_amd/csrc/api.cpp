@@ -248,7 +248,9 @@ ba_status ba_cache_append_batched(const ba_ring* ring, const void* k, const void
 
 int32_t ba_attention_query_tile(int32_t head_dim, int32_t dtype, int32_t max_keys) {
   if ((head_dim != 64 && head_dim != 128) || max_keys < 0) return 0;
-  if (dtype == BA_BF16) return ba::attention_bf16_q_tile(head_dim, ba::attention_bf16_shape(head_dim, max_keys));
+  if (dtype == BA_BF16)
+    return ba::attention_bf16_q_tile(head_dim, ba::attention_bf16_shape(head_dim, max_keys,
+                                                                        (max_keys + ba::kKeyTile - 1) / ba::kKeyTile));
   if (dtype == BA_F32) return ba::attention_f32_q_tile();
   return 0;
 }
@@ -260,7 +262,7 @@ size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_b
   // two partial results per tail workgroup, one tail workgroup per resident
   // slot; enough for either launch shape
   size_t bytes = 0;
-  for (int shape = 0; shape < (head_dim == 64 ? 2 : 1); ++shape) {
+  for (int shape = 0; shape < (head_dim == 64 ? 2 : 1); ++shape) {   // the resident shape takes none
     int wg = 0;
     if (resident_workgroups(head_dim, shape, &wg) != hipSuccess || wg < 1) return 0;
     const size_t b = (size_t)2 * (wg / 8 * 8) * ba::attention_partial_bytes(head_dim, shape);
@@ -369,16 +371,31 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
     // this launch's segment tables (checked above); launch shape from its
     // longest key set
     ba::AttnBlock tables[ba::kAttnMaxBlocks];
-    int64_t max_keys = 0;
+    int64_t max_keys = 0, max_tiles = 0;
     for (int i = 0; i < nb; ++i) {
-      int64_t keys = 0;
+      int64_t keys = 0, tiles = 0;
       block_table(meta[first + i], first + i, q_stride, cache, text, &tables[i], &keys);
       if (keys > max_keys) max_keys = keys;
+      if (keys > 0)
+        for (int sg = 0; sg < tables[i].n_segs; ++sg) tiles += (tables[i].len[sg] + ba::kKeyTile - 1) / ba::kKeyTile;
+      if (tiles > max_tiles) max_tiles = tiles;
     }
-    const int shape = bf16 ? ba::attention_bf16_shape(D, max_keys) : 0;
+    int shape = bf16 ? ba::attention_bf16_shape(D, max_keys, max_tiles) : 0;
+    if (shape == 2) {
+      // the resident shape pays a key-set copy per workgroup up front: with
+      // fewer units of 32 queries than the device has wave slots (measured:
+      // 1512 and 2256 units on 3072 slots ran 15-19 % slower than the narrow
+      // shape, 3072 and more 4-15 % faster) the narrow shape is taken
+      int64_t units = 0;
+      for (int i = 0; i < nb; ++i) units += (int64_t)H * ((tables[i].q_len + 31) / 32);
+      int wg = 0;
+      hipError_t e = resident_workgroups(D, shape, &wg);
+      if (e != hipSuccess && !plan) return hip_fail(e, "device query");
+      if (e == hipSuccess && units < (int64_t)wg * ba::kResWaves) shape = 1;
+    }
     const int qtile = bf16 ? ba::attention_bf16_q_tile(D, shape) : ba::attention_f32_q_tile();
     int resident = 0;   // workgroups the device holds at once (split schedule)
-    if (bf16 && has_workspace) {
+    if (bf16 && has_workspace && shape != 2) {
       hipError_t e = resident_workgroups(D, shape, &resident);
       if (e != hipSuccess) return hip_fail(e, "device query");
     }
@@ -464,6 +481,17 @@ ba_status attention_run(const void* q, int32_t q_stride, const ba_ring* cache, c
     if (plan) {
       if (a.tail_wg > *plan) *plan = a.tail_wg;
       continue;
+    }
+    if (shape == 2) {
+      // resident key sets: the units (tasks of 32 queries) in equal
+      // contiguous ranges, one per workgroup the device holds at once (no
+      // workspace)
+      int wg = 0;
+      hipError_t e = resident_workgroups(D, shape, &wg);
+      if (e != hipSuccess) return hip_fail(e, "device query");
+      if (wg < 8) wg = 8;
+      const int64_t per_xcd = ((tasks < wg ? tasks : wg) + 7) / 8;
+      a.wg_per_xcd = (int32_t)per_xcd;
     }
     hipError_t e = bf16 ? ba::launch_attention_bf16(a, D, shape, stream) : ba::launch_attention_f32(a, D, stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");

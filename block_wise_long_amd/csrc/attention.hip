@@ -133,11 +133,14 @@ struct WaveState {
 // shape: one workgroup per CU, as many queries as the registers allow sharing
 // each K/V tile copy; D = 64: 12 waves, 3 per SIMD; D = 128: 8 waves, 2 per
 // SIMD.  S = 1, the narrow shape for short key sets (D = 64 only): 4 waves,
-// three workgroups per CU, whose prologues and epilogues overlap.  KW of the
-// waves copy the K tile, the others the V^T tile (see load_tile).
+// three workgroups per CU, whose prologues and epilogues overlap.  S = 2,
+// the resident shape for key sets held whole in LDS (see
+// attention_resident_kernel): one workgroup per CU.  KW of the waves copy the
+// K tile, the others the V^T tile (see load_tile).
 template <int D, int S = 0> struct Shape;
 template <> struct Shape<64, 0> { static constexpr int NW = 12, WAVES_PER_SIMD = 3, KW = 8; };
 template <> struct Shape<64, 1> { static constexpr int NW = 4, WAVES_PER_SIMD = 3, KW = 2; };
+template <> struct Shape<64, 2> { static constexpr int NW = kResWaves, WAVES_PER_SIMD = 3, KW = 8; };
 template <> struct Shape<128, 0> { static constexpr int NW = 8, WAVES_PER_SIMD = 2, KW = 4; };
 
 constexpr int kBuffers = 3;   // LDS tile buffers: in use, being consumed, being filled
@@ -890,6 +893,162 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, Tile<D, S>::THREADS))) 
 }
 
 // ---------------------------------------------------------------------------
+// Resident key sets (head dim 64, at most kResTiles tiles of 64 keys): a text
+// prompt's K/V (the separate text cross-attention) or any other short key
+// set.  A workgroup copies the whole key set of one (block, head) into LDS
+// once and its waves then run independent units of 32 queries against it,
+// with no barrier inside a unit: the per-tile copies, barriers and pipeline
+// refills of the streaming kernel would otherwise recur every few tiles.
+//
+// Work: the launch's units in (block, head, 32-query unit) order, cut into
+// one contiguous range per workgroup; the ranges of XCD x are consecutive, so
+// that an XCD's workgroups share few key sets in its L2.  A range that crosses
+// a (block, head) boundary runs one phase per key set: barrier, copy, barrier,
+// units dealt round-robin to the waves (wave i takes units i, i + NW, ...;
+// the hardware places wave i on SIMD i % 4, so the SIMDs get equal shares).
+// Units are never cut: measured at 5400 queries x 24 heads, sharing the
+// left-over units' tiles among groups of waves (partial states folded in LDS
+// or through memory) was slower than letting one wave run a unit alone.
+// LDS: a zero tile, the key set's tiles, and one more tile that only the
+// discarded look-ahead of the last step reads.
+// ---------------------------------------------------------------------------
+constexpr int kResBufs = kResTiles + 2;
+
+template <int S>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Tile<64, S>::THREADS)))
+__attribute__((amdgpu_waves_per_eu(Shape<64, S>::WAVES_PER_SIMD, Shape<64, S>::WAVES_PER_SIMD)))
+void attention_resident_kernel(const AttnArgs a) {
+  constexpr int D = 64;
+  using T = Tile<D, S>;
+  constexpr int NKS = D / 16;
+  constexpr int NOB = D / 32;
+  // res[0]: zeros (the first step's deferred PV); res[1 + t]: tile t
+  __shared__ u32x4 res[kResBufs][T::CH];
+  static_assert(sizeof(res) <= 160 * 1024, "LDS");
+  const unsigned lds_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)&res[0][0];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const CopyLane cl = copy_lane<D, S>(wave_u, lane);
+  const float c = a.qscale;
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < T::LOADS; ++u)
+      if (T::CH % T::THREADS == 0 || u * T::THREADS + tid < T::CH) res[0][u * T::THREADS + tid] = z;
+  }
+  const int n_wg = 8 * a.wg_per_xcd;
+  const int j = (blockIdx.x & 7) * a.wg_per_xcd + (blockIdx.x >> 3);
+  int pos = split_start(a.n_tasks, n_wg, j);
+  const int end = split_start(a.n_tasks, n_wg, j + 1);
+  const bf16x8 sel = row_sum_selector(lane);
+
+  while (pos < end) {
+    // the phase: units [u0, u0 + n) of (block b, head h)
+    int b = 0;
+    while (b + 1 < a.n_blocks && a.blk[b + 1].task_start <= pos) ++b;
+    const AttnBlock& B = a.blk[b];
+    const int r = pos - B.task_start;
+    const int h = r / B.nqt;
+    const int u0 = r - h * B.nqt;
+    const int n = end - pos < B.nqt - u0 ? end - pos : B.nqt - u0;
+    const int n_tiles = B.n_tiles;
+
+    // copy the key set (every wave's reads of the previous one are done);
+    // vt packs each tile's count of keys before its segment's end, capped
+    // at 64, in 7 bits
+    __syncthreads();
+    uint64_t vt = 0;
+    {
+      Cursor lc;
+      lc.seg = 0;
+      open_segment<D>(a, B, h, lc);
+      for (int t = 0; t < n_tiles; ++t) {
+        const int v = lc.len - lc.off;
+        vt |= (uint64_t)(v < kKTile ? v : kKTile) << (7 * t);
+        load_tile<D, S>(lc, cl, wave_u, lds_addr + 16u * T::CH * (1 + t));
+        if (t + 1 < n_tiles) advance<D>(a, B, h, lc);
+      }
+    }
+    wait_loads();
+    __syncthreads();
+
+    for (int i = wave_u; i < n; i += T::NW) {
+      const int qrow = (u0 + i) * 32 + (lane & 31);
+      const bool row_ok = qrow < B.q_len;
+      const int qrow_c = row_ok ? qrow : B.q_len - 1;
+      bf16x8 qf[NKS];
+      {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                             (((int64_t)b * a.q_stride + qrow_c) * a.heads + h) * D;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+          qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * half));
+      }
+      // fast form first; the exact one if this wave's weights overflowed
+      for (int exact = 0; exact < 2; ++exact) {
+        WaveState<D> w;
+#pragma unroll
+        for (int jj = 0; jj < NOB; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) w.o[jj][e] = 0.f;
+        w.l_sum = 0.f;
+        w.l_acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x16 sa, sb;
+        bf16x8 p[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[k2][e] = (__bf16)0.0f;
+        sa = scores<D>(res[1], lane, 0, qf);
+        w.m_ref = first_reference(sa, c, (int)(vt & 127));
+        // A run of tiles from `base` = the LDS buffer before the first: the
+        // previous, current and next buffers of each tile sit at fixed
+        // offsets from it (every operand address is a per-lane base plus an
+        // immediate).  Two tiles per round, then the odd one.
+        auto tile = [&](const u32x4* base, auto k_c, int t) {
+          constexpr int k = decltype(k_c)::value;
+          const int valid = (int)((vt >> (7 * t)) & 127);
+          pipe_step<D>(base + (k + 1) * T::CH, 1, base + k * T::CH, 1, lane, qf, c, sa, sb, p, valid,
+                       exact != 0, sel, w);
+          pipe_step<D>(base + (k + 2) * T::CH, 0, base + (k + 1) * T::CH, 0, lane, qf, c, sb, sa, p,
+                       valid - 32, exact != 0, sel, w);
+        };
+        int t = 0;
+        for (; t + 2 <= n_tiles; t += 2) {
+          const u32x4* base = res[t];
+          tile(base, std::integral_constant<int, 0>{}, t);
+          tile(base, std::integral_constant<int, 1>{}, t + 1);
+        }
+        if (t < n_tiles) tile(res[t], std::integral_constant<int, 0>{}, t);
+        // the last group's PV (group 1 of the last tile)
+        accumulate<D>(res[n_tiles], lane, 1, p, w.o);
+        w.l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p[0], w.l_acc, 0, 0, 0);
+        w.l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p[1], w.l_acc, 0, 0, 0);
+        w.l_sum = row_sum_of_lane(w.l_acc, lane);
+        if (!exact) {
+          // overflow check of the fast form, as in the streaming kernel, but
+          // per wave: the key set in LDS is read-only, so a wave can run its
+          // unit again alone
+          float chk = w.l_sum;
+#pragma unroll
+          for (int jj = 0; jj < NOB; ++jj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) chk += w.o[jj][e];
+          const bool bad = !(__builtin_isfinite(chk) && w.l_sum < 0x1p100f);
+          if (__builtin_amdgcn_ballot_w64(bad) != 0) continue;
+        }
+        store_output<D>(a, b, h, qrow, row_ok, half, w);
+        break;
+      }
+    }
+    pos += n;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: one query per lane, exact running maximum, VALU only.
 // ---------------------------------------------------------------------------
 constexpr int kF32QTile = 64;
@@ -973,12 +1132,14 @@ __global__ __launch_bounds__(kF32QTile) void attention_f32_kernel(const AttnArgs
 
 }  // namespace
 
-// shape: 0 wide, 1 narrow (head_dim 64 only)
+// shape: 0 wide, 1 narrow, 2 resident (head_dim 64 only)
 int attention_bf16_q_tile(int head_dim, int shape) {
-  return head_dim == 128 ? Tile<128, 0>::QTILE : shape ? Tile<64, 1>::QTILE : Tile<64, 0>::QTILE;
+  if (head_dim == 128) return Tile<128, 0>::QTILE;
+  return shape == 2 ? 32 : shape ? Tile<64, 1>::QTILE : Tile<64, 0>::QTILE;
 }
 int attention_f32_q_tile() { return kF32QTile; }
 size_t attention_partial_bytes(int head_dim, int shape) {
+  if (shape == 2) return 0;     // pieces are folded in LDS
   return sizeof(float) *
          (head_dim == 128 ? Partial<128, 0>::FLOATS : shape ? Partial<64, 1>::FLOATS : Partial<64, 0>::FLOATS);
 }
@@ -986,6 +1147,8 @@ size_t attention_partial_bytes(int head_dim, int shape) {
 hipError_t attention_bf16_resident(int head_dim, int shape, int* per_cu) {
   if (head_dim == 128)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<128, 0>, Tile<128, 0>::THREADS, 0);
+  if (shape == 2)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_resident_kernel<2>, Tile<64, 2>::THREADS, 0);
   if (shape)
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<64, 1>, Tile<64, 1>::THREADS, 0);
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, attention_bf16_kernel<64, 0>, Tile<64, 0>::THREADS, 0);
@@ -1004,6 +1167,10 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention_bf16(const AttnArgs& a, int head_dim, int shape, hipStream_t s) {
   if (head_dim == 128) return launch_shape<128, 0>(a, s);
+  if (shape == 2) {
+    hipLaunchKernelGGL(attention_resident_kernel<2>, dim3(8 * a.wg_per_xcd), dim3(Tile<64, 2>::THREADS), 0, s, a);
+    return hipGetLastError();
+  }
   return shape ? launch_shape<64, 1>(a, s) : launch_shape<64, 0>(a, s);
 }
 

@@ -122,14 +122,21 @@ __host__ __device__ inline XcdPlan xcd_plan(const AttnArgs& a, int x) {
 }
 hipError_t launch_attention_f32(const AttnArgs& a, int head_dim, hipStream_t s);
 // Launch shape of the bf16 kernel for a launch whose longest key set has
-// max_keys keys: 1 (narrow: 4-wave workgroups, several per CU) for short key
-// sets at head_dim 64, where the per-task prologue and epilogue weigh most;
-// else 0 (wide: one workgroup per CU sharing each K/V copy among the most
-// queries).  Measured at the 480p query shape: narrow 10-20 % faster up to
-// 3072 keys, wide 2.5 % faster at 4096.
+// max_keys keys and whose key sets span at most max_tiles tiles of 64 keys
+// (tiles never straddle segments): 2 (resident: the whole key set held in
+// LDS, independent 32-query units) when head_dim is 64 and every key set fits
+// kResTiles tiles; 1 (narrow: 4-wave workgroups, several per CU) for other
+// short key sets at head_dim 64, where the per-task prologue and epilogue
+// weigh most; else 0 (wide: one workgroup per CU sharing each K/V copy among
+// the most queries).  Measured at the 480p query shape: narrow 10-20 %
+// faster up to 3072 keys, wide 2.5 % faster at 4096.
+constexpr int kResTiles = 8;
+constexpr int kResWaves = 12;            // waves per workgroup of the resident shape
 constexpr int64_t kNarrowMaxKeys = 3072;
-inline int attention_bf16_shape(int head_dim, int64_t max_keys) {
-  return head_dim == 64 && max_keys <= kNarrowMaxKeys ? 1 : 0;
+inline int attention_bf16_shape(int head_dim, int64_t max_keys, int64_t max_tiles) {
+  if (head_dim != 64) return 0;
+  if (max_tiles <= kResTiles) return 2;
+  return max_keys <= kNarrowMaxKeys ? 1 : 0;
 }
 int attention_bf16_q_tile(int head_dim, int shape);   // queries per workgroup of the bf16 kernel
 size_t attention_partial_bytes(int head_dim, int shape);   // workspace bytes of one partial result

@@ -164,7 +164,8 @@ typedef struct {
  *          24 key tiles of 64 per tail workgroup, e.g. a text-only key set)
  *          and when whole query tiles would leave less than a quarter of an
  *          XCD's workgroup slots idle in their last round;
- *          ba_attention_plan tells which schedule a call takes.
+ *          ba_attention_plan tells which schedule a call takes.  A launch
+ *          of the resident shape (see ba_attention_query_tile) uses none.
  *          Results agree to rounding either way and are deterministic.  Its
  *          contents need no initialisation; calls that share a workspace must
  *          be ordered on one stream.
@@ -207,10 +208,16 @@ size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_b
 /* Queries of one head that one workgroup of ba_block_attention takes (its
  * query tile) in a launch whose longest key set (cache segments + text) has
  * max_keys keys: a block of q_len queries is heads * ceil(q_len / tile)
- * tasks.  bf16, head_dim 64: 128 up to 3072 keys (short key sets, several
- * workgroups per CU), else 384; head_dim 128: 256; fp32: 64.  A call covers
- * its blocks in launches of up to 16.  0 for a head_dim / dtype pair the call
- * does not support or max_keys < 0.  Needs no device. */
+ * tasks.  bf16, head_dim 64: 32 up to 512 keys (the resident shape: each
+ * workgroup holds one head's whole key set in LDS and its waves take units
+ * of 32 queries), 128 up to 3072 keys (short key sets, several workgroups
+ * per CU), else 384; head_dim 128: 256; fp32: 64.  A launch with key sets of
+ * at most 512 keys takes the resident shape only when every key set spans at
+ * most 8 tiles of 64 keys (tiles do not cross segments) and it has at least
+ * as many 32-query units as the device has wave slots for it (12 per CU);
+ * else it takes the 128-query shape.  A call covers its blocks in launches of
+ * up to 16.  0 for a head_dim / dtype pair the call does not support or
+ * max_keys < 0.  Needs no device. */
 int32_t ba_attention_query_tile(int32_t head_dim, int32_t dtype, int32_t max_keys);
 
 /* The schedule ba_block_attention would take for these arguments and a

@@ -32,6 +32,7 @@ def _fill(w, rng, lens, H, D, dtype, std, text_len):
     (128, (128, 128), 16),       # exact tiles
     (1, (1,), 0),                # a single query over a single key
     (257, (64, 65, 63), 64),     # tile-boundary lengths
+    (300, (200, 200, 150), 37),  # 12 key tiles: past the resident limit at head dim 64
 ])
 def test_bf16_parity_small(D, q_len, lens, text_len):
     rng = _rng(D * 1000 + q_len)
