@@ -3,6 +3,7 @@
 // Every check runs before anything is enqueued; on failure nothing is
 // enqueued, no descriptor changes and ba_last_error() says why.
 #include <math.h>
+#include <atomic>
 #include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
@@ -132,13 +133,38 @@ void coefficients(const std::vector<double>& ab, int stride, int t, float* c1, f
 }
 
 // Workgroups of the bf16 attention kernel (launch shape `shape`) the current
-// device holds at once.
+// device holds at once.  The answer depends only on the device and the
+// kernel, so it is asked once per (device, head dim, shape) and kept.
+constexpr int kCachedDevices = 64;
+std::atomic<int> g_resident[kCachedDevices][2][3];
+std::once_flag g_resident_init;
+
 hipError_t resident_workgroups(int head_dim, int shape, int* n) {
-  int dev = 0, cus = 0, per_cu = 0;
+  std::call_once(g_resident_init, [] {
+    for (auto& d : g_resident)
+      for (auto& h : d)
+        for (auto& x : h) x.store(-1, std::memory_order_relaxed);
+  });
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) {
+    *n = 0;
+    return e;
+  }
+  std::atomic<int>* slot =
+      dev >= 0 && dev < kCachedDevices && shape >= 0 && shape < 3 ? &g_resident[dev][head_dim == 128][shape] : nullptr;
+  if (slot != nullptr) {
+    const int v = slot->load(std::memory_order_acquire);
+    if (v >= 0) {
+      *n = v;
+      return hipSuccess;
+    }
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) e = ba::attention_bf16_resident(head_dim, shape, &per_cu);
   *n = e == hipSuccess ? cus * per_cu : 0;
+  if (e == hipSuccess && slot != nullptr) slot->store(*n, std::memory_order_release);
   return e;
 }
 
