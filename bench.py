@@ -353,9 +353,9 @@ def queue_bench(args):
         ang = (pos * freq).t()
         layer = {"w": w, "rope": torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).contiguous()}
     fq = FifoQueue(lat, tk, tv, T=T, layer=layer)
-    for _ in range(max(args.warmup, 1)):      # from step 1 on every block has its neighbour's context
-        fq.step(noise)
-    torch.cuda.synchronize()
+    # from step 1 on every block has its neighbour's context; the warm-up
+    # also lasts long enough for the shader clock to ramp up
+    warm_up(torch, lambda: fq.step(noise), max(args.warmup, 1), args.warmup_min_s)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -400,9 +400,7 @@ def project_bench(args):
     k = torch.empty((1, L, H, D), dtype=torch.bfloat16, device="cuda")
 
     def timed(fn):
-        for _ in range(max(args.warmup, 1)):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(torch, fn, max(args.warmup, 1), args.warmup_min_s)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
@@ -460,9 +458,7 @@ def noise_bench(args):
         microseconds of kernel time); with a flush, the Infinity Cache is
         overwritten before each call."""
         reps = args.steps if reps is None else reps
-        for _ in range(max(args.warmup, 1)):
-            B.ba_noise_block(pool, frames, out)
-        torch.cuda.synchronize()
+        warm_up(torch, lambda: B.ba_noise_block(pool, frames, out), max(args.warmup, 1), args.warmup_min_s)
         ts = []
         for _ in range(reps):
             if flush is not None:

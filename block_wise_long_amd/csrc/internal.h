@@ -179,7 +179,7 @@ hipError_t launch_project(const ProjArgs& a, int head_dim, hipStream_t s);
 #define BA_PROJ_WAVES_T 4
 #endif
 #ifndef BA_PROJ_STAGES
-#define BA_PROJ_STAGES 3
+#define BA_PROJ_STAGES 4
 #endif
 #ifndef BA_PROJ_GROUP
 #define BA_PROJ_GROUP 8

@@ -111,6 +111,15 @@ __device__ __forceinline__ void load_stage(const ProjArgs& a, const uint16_t* xb
 
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
+// Workgroup barrier that orders LDS accesses only.  The fence of
+// __syncthreads also waits for every global load in flight, which would
+// drain the LDS-direct copies of the stages not yet due at every stage.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wait until at most n stages' loads (n * kLoads) are still in flight: loads
 // complete in order, so every older stage has landed.  simm16 of s_waitcnt:
 // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 (the latter two left at
@@ -201,7 +210,7 @@ void project_kernel(const ProjArgs a) {
     const int issued = n_k < kStages - 1 ? n_k : kStages - 1;
     wait_newer(issued - 1);                             // stage 0 has landed
   }
-  __syncthreads();
+  lds_barrier();
 
   bf16x8 fw[2][kRB], fx[2][kTB];
   auto read_frag = [&](int f, const u32x4* L, int ks) {
@@ -230,7 +239,7 @@ void project_kernel(const ProjArgs a) {
         // MFMAs, so that buffer takes stage kt + kStages - 1
         const int ahead = kt + kStages - 2;               // newest stage issued so far
         wait_newer((ahead < n_k ? ahead : n_k - 1) - (kt + 1));
-        __syncthreads();
+        lds_barrier();
         if (kt + kStages - 1 < n_k)
           load_stage(a, xb, loff, (kt + kStages - 1) * kKStep, tid,
                      lds_addr + 16u * kStageChunks * ((kt + kStages - 1) % kStages));
