@@ -170,7 +170,7 @@ hipError_t launch_project(const ProjArgs& a, int head_dim, hipStream_t s);
 #define BA_PROJ_CH 256
 #endif
 #ifndef BA_PROJ_K
-#define BA_PROJ_K 32
+#define BA_PROJ_K 64
 #endif
 #ifndef BA_PROJ_WPS
 #define BA_PROJ_WPS 2
@@ -179,7 +179,7 @@ hipError_t launch_project(const ProjArgs& a, int head_dim, hipStream_t s);
 #define BA_PROJ_WAVES_T 4
 #endif
 #ifndef BA_PROJ_STAGES
-#define BA_PROJ_STAGES 4
+#define BA_PROJ_STAGES 2
 #endif
 #ifndef BA_PROJ_GROUP
 #define BA_PROJ_GROUP 8

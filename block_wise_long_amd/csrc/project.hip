@@ -130,18 +130,18 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(v < 64, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (v & 15) | ((v >> 4) << 14));
 }
-__device__ __forceinline__ void wait_newer(int n) {   // n in [0, kStages - 2]
+__device__ __forceinline__ void wait_newer(int n) {   // n in [0, kStages - 1]
   switch (n) {
     case 0: wait_vm<0>(); break;
-    case 1: wait_vm<1>(); break;
-    case 2: if constexpr (kStages > 3) wait_vm<2>(); break;
-    case 3: if constexpr (kStages > 4) wait_vm<3>(); break;
-    case 4: if constexpr (kStages > 5) wait_vm<4>(); break;
-    case 5: if constexpr (kStages > 6) wait_vm<5>(); break;
+    case 1: if constexpr (kStages > 1) wait_vm<1>(); break;
+    case 2: if constexpr (kStages > 2) wait_vm<2>(); break;
+    case 3: if constexpr (kStages > 3) wait_vm<3>(); break;
+    case 4: if constexpr (kStages > 4) wait_vm<4>(); break;
+    case 5: if constexpr (kStages > 5) wait_vm<5>(); break;
     default: wait_vm<0>(); break;
   }
 }
-static_assert(kStages >= 3 && kStages <= 7, "stages: the next stage is issued a full stage before it is published");
+static_assert(kStages >= 2 && kStages <= 6, "stages");
 
 // Workgroup -> output tile.  Workgroup w runs on XCD w % 8, whose L2 is its
 // own; XCD x takes a contiguous run of tiles in an order that walks bands of
@@ -204,10 +204,10 @@ void project_kernel(const ProjArgs a) {
   // sets), and the barrier that publishes the next stage sits between the two,
   // so a wave's MFMA stream never waits on its own LDS reads.
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
+  for (int s = 0; s < kStages; ++s)
     if (s < n_k) load_stage(a, xb, loff, s * kKStep, tid, lds_addr + 16u * kStageChunks * s);
   {
-    const int issued = n_k < kStages - 1 ? n_k : kStages - 1;
+    const int issued = n_k < kStages ? n_k : kStages;
     wait_newer(issued - 1);                             // stage 0 has landed
   }
   lds_barrier();
@@ -234,15 +234,14 @@ void project_kernel(const ProjArgs a) {
         read_frag(nxt, L, ks + 1);
       } else if constexpr (!decltype(is_last)::value) {
         // publish stage kt + 1 (the stages issued after it may stay in
-        // flight); past the barrier every wave has finished iteration kt - 1,
-        // whose reads of buffer (kt - 1) mod kStages all completed before its
-        // MFMAs, so that buffer takes stage kt + kStages - 1
-        const int ahead = kt + kStages - 2;               // newest stage issued so far
+        // flight); past the barrier every wave's reads of this stage's buffer
+        // are done (its last operands are already in registers), so that
+        // buffer takes stage kt + kStages
+        const int ahead = kt + kStages - 1;               // newest stage issued so far
         wait_newer((ahead < n_k ? ahead : n_k - 1) - (kt + 1));
         lds_barrier();
-        if (kt + kStages - 1 < n_k)
-          load_stage(a, xb, loff, (kt + kStages - 1) * kKStep, tid,
-                     lds_addr + 16u * kStageChunks * ((kt + kStages - 1) % kStages));
+        if (kt + kStages < n_k)
+          load_stage(a, xb, loff, (kt + kStages) * kKStep, tid, lds_addr + 16u * kStageChunks * (kt % kStages));
         read_frag(nxt, lds[(kt + 1) % kStages], 0);
       }
       __builtin_amdgcn_sched_barrier(0);
