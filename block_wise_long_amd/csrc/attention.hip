@@ -13,7 +13,9 @@
 //     All waves of a workgroup share each K/V tile copied to LDS.  Wide
 //     shape: 12 waves (384 queries) at head dim 64, 8 waves (256) at 128, one
 //     workgroup per CU; narrow shape for short key sets (head dim 64): 4
-//     waves, three workgroups per CU (see Shape).
+//     waves, three workgroups per CU (see Shape).  Key sets of at most 8
+//     tiles at head dim 64 (a text prompt) take attention_resident_kernel
+//     instead: the whole key set in LDS, waves on independent 32-query units.
 //   * S^T = K Q^T is computed per 32-key group, so that a lane owns one
 //     query column and 16 of its scores: every per-query softmax quantity is
 //     lane-local (lanes l and l^32 share a query), and O^T = V^T P^T leaves the
