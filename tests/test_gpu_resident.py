@@ -142,3 +142,27 @@ def test_same_bits_as_the_streaming_kernel():
     ref, _ = w.oracle(q, [m0, m9], heads=heads, rows=rows)
     got = decode(out_s, "bf16")
     _bar(got[:, rows][:, :, heads], ref[:, rows][:, :, heads])
+
+
+def test_eight_tiles_from_four_segments():
+    # the largest resident key set, made of three cache segments and the text
+    # (128 + 64 + 100 + 140 keys: 2 + 1 + 2 + 3 = 8 tiles, a partial tile
+    # inside the key set and one at its end); 16 heads x 6144 queries
+    import block_wise_long_amd as B
+    rng = _rng(85)
+    H, D, L = 16, 64, 6144
+    _resident(H * L // 32)
+    w = Workload("bf16", 3, 128, H, D, 140)
+    for n in (128, 64, 100):
+        w.append(draw(rng, (n, H, D), 0.5, "bf16"), draw(rng, (n, H, D), 0.5, "bf16"))
+    w.set_text(draw(rng, (140, H, D), 0.5, "bf16"), draw(rng, (140, H, D), 0.5, "bf16"))
+    metas = [{"q_len": L, "segs": [(0, 128), (1, 64), (2, 100)], "text_slot": 0, "text_len": 140}]
+    assert B.ba_attention_query_tile(D, B.BA_BF16, 432) == 32
+    q = draw(rng, (1, L, H, D), 0.5, "bf16")
+    out, lse = w.run(q, metas)
+    heads, rows = [0, 7, 15], sorted(set(range(0, L, 41)) | set(range(L - 40, L)))
+    ref, ref_lse = w.oracle(q, metas, heads=heads, rows=rows)
+    got = decode(out, "bf16")
+    _bar(got[:, rows][:, :, heads], ref[:, rows][:, :, heads])
+    sel = ~np.isnan(ref_lse)
+    assert np.max(np.abs(lse.cpu().numpy()[sel] - ref_lse[sel])) < 2e-3
