@@ -90,6 +90,41 @@ def test_batched_blocks_with_different_key_sets():
     assert np.isnan(got[1, 129:]).all() and np.isnan(got[2]).all() and np.isnan(got[4, 17:]).all()
 
 
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_eight_segments_per_block(D, dtype):
+    # the most cache segments a block takes, in an order unlike their slots'
+    # and after a FIFO wrap (11 appends into 9 slots), one of them empty,
+    # lengths at and around tile edges, plus the text (13 key tiles); a
+    # second block of eight one-key segments and no text (8 one-key tiles)
+    import block_wise_long_amd as B
+    rng = _rng(880 + D + (dtype == "f32"))
+    H = 2
+    std = 0.5 if dtype == "bf16" else 1.0
+    w = Workload(dtype, 9, 130, H, D, 40)
+    held = {}
+    for n in (130, 1, 63, 64, 65, 129, 17, 100, 128, 77, 33):
+        held[w.append(draw(rng, (n, H, D), std, dtype), draw(rng, (n, H, D), std, dtype))] = n
+    assert held == {0: 77, 1: 33, 2: 63, 3: 64, 4: 65, 5: 129, 6: 17, 7: 100, 8: 128}
+    w.set_text(draw(rng, (40, H, D), std, dtype), draw(rng, (40, H, D), std, dtype))
+    segs0 = [(5, 129), (0, 77), (8, 128), (3, 64), (6, 0), (2, 63), (4, 65), (1, 33)]
+    segs1 = [(s, 1) for s in (7, 0, 6, 1, 5, 2, 4, 3)]
+    assert len(segs0) == len(segs1) == B.BA_MAX_SEGS
+    metas = [{"q_len": 300, "segs": segs0, "text_slot": 0, "text_len": 40},
+             {"q_len": 45, "segs": segs1, "text_slot": 0, "text_len": 0}]
+    q = draw(rng, (2, 300, H, D), std, dtype)
+    out, lse = w.run(q, metas)
+    ref, ref_lse = w.oracle(q, metas)
+    got = decode(out, dtype)
+    check_contract(got, ref, dtype, gate2=False)
+    if dtype == "bf16":
+        rms = math.sqrt(np.nanmean(ref ** 2))
+        assert np.nanmax(np.abs(got - ref)) <= 2 ** -7 * np.nanmax(np.abs(ref)) + 0.05 * rms
+    sel = ~np.isnan(ref_lse)
+    assert np.max(np.abs(lse.cpu().numpy()[sel] - ref_lse[sel])) < (1e-5 if dtype == "f32" else 2e-3)
+    assert np.isnan(got[1, 45:]).all()
+
 def _needle_case(D, slot_of_needle, pos, text=False):
     """One key aligned with every query, huge gap to all others: output = that key's V."""
     H, n_slots, L = 2, 3, 150

@@ -166,3 +166,30 @@ def test_eight_tiles_from_four_segments():
     _bar(got[:, rows][:, :, heads], ref[:, rows][:, :, heads])
     sel = ~np.isnan(ref_lse)
     assert np.max(np.abs(lse.cpu().numpy()[sel] - ref_lse[sel])) < 2e-3
+
+
+def test_eight_segments_in_one_resident_key_set():
+    # the most cache segments a block takes, one of them empty, each at most
+    # one tile, in an order unlike their slots', plus a text of 30 keys:
+    # 7 + 1 = 8 tiles, every one of them partial but two
+    import block_wise_long_amd as B
+    rng = _rng(86)
+    H, D, L = 16, 64, 6144
+    _resident(H * L // 32)
+    w = Workload("bf16", 8, 64, H, D, 30)
+    lens = (64, 1, 63, 33, 64, 17, 40, 5)
+    for n in lens:
+        w.append(draw(rng, (n, H, D), 0.5, "bf16"), draw(rng, (n, H, D), 0.5, "bf16"))
+    w.set_text(draw(rng, (30, H, D), 0.5, "bf16"), draw(rng, (30, H, D), 0.5, "bf16"))
+    segs = [(6, 40), (0, 64), (3, 33), (7, 0), (1, 1), (5, 17), (4, 64), (2, 63)]
+    assert len(segs) == B.BA_MAX_SEGS
+    metas = [{"q_len": L, "segs": segs, "text_slot": 0, "text_len": 30}]
+    assert B.ba_attention_query_tile(D, B.BA_BF16, sum(n for _, n in segs) + 30) == 32
+    q = draw(rng, (1, L, H, D), 0.5, "bf16")
+    out, lse = w.run(q, metas)
+    heads, rows = [0, 8, 15], sorted(set(range(0, L, 43)) | set(range(L - 33, L)))
+    ref, ref_lse = w.oracle(q, metas, heads=heads, rows=rows)
+    got = decode(out, "bf16")
+    _bar(got[:, rows][:, :, heads], ref[:, rows][:, :, heads])
+    sel = ~np.isnan(ref_lse)
+    assert np.max(np.abs(lse.cpu().numpy()[sel] - ref_lse[sel])) < 2e-3
