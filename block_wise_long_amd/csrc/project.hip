@@ -268,6 +268,27 @@ void project_kernel(const ProjArgs a) {
   const int HD = a.heads * D;
   const int tok_w = t0 + kWaveToks * tw;               // first token of the wave's columns
   uint16_t* E = reinterpret_cast<uint16_t*>(&lds[0][0]) + wave * kEpiWaveElems;
+  // Rotation table entries of the wave's tokens, all issued together (one
+  // memory round trip).  At head dim 64 every unit is a whole head (pairs
+  // 0..31), so the wave loads them once; at 128 a unit is half a head and
+  // loads its own half.  Tokens past the end read the last token's entry
+  // (their results are replaced by zeros).
+  float2 cs[2][kTB][8];
+  auto load_cs = [&](int dbase) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int tb = 0; tb < kTB; ++tb) {
+        const int tok = tok_w + 32 * tb + (lane & 31);
+        const int tc = tok < a.n_tokens ? tok : a.n_tokens - 1;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const int d = dbase + 32 * c2 + 8 * (i >> 2) + 4 * half + (i & 3);
+          cs[c2][tb][i >> 1] = *reinterpret_cast<const float2*>(ropeb + ((int64_t)(d >> 1) * a.n_tokens + tc) * 2);
+        }
+      }
+  };
+  if (D == 64 && ropeb != nullptr) load_cs(0);
 #pragma unroll
   for (int u = 0; u < kWaveRows / 64; ++u) {
     const int r0 = ch0 + kWaveRows * cw + 64 * u;      // first row of the unit
@@ -277,6 +298,7 @@ void project_kernel(const ProjArgs a) {
     const int dbase = r0 - which * HD - h * D;         // 0, or 64 in a 128-dim head
     if (which == 0 && qb == nullptr) continue;
     const bool rotate = which < 2 && ropeb != nullptr;
+    if (D == 128 && rotate) load_cs(dbase);
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
@@ -290,11 +312,10 @@ void project_kernel(const ProjArgs a) {
           // is pair-major, so the lanes (consecutive tokens) read one run
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
-            const int d = dbase + 32 * c2 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const float2 cs = *reinterpret_cast<const float2*>(ropeb + ((int64_t)(d >> 1) * a.n_tokens + tok) * 2);
+            const float2 r = cs[c2][tb][i >> 1];
             const float y0 = y[i], y1 = y[i + 1];
-            y[i] = y0 * cs.x - y1 * cs.y;
-            y[i + 1] = y0 * cs.y + y1 * cs.x;
+            y[i] = y0 * r.x - y1 * r.y;
+            y[i + 1] = y0 * r.y + y1 * r.x;
           }
         }
         if (!valid) {
