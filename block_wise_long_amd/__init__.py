@@ -75,6 +75,11 @@ _SIGS = {
     "ba_block_attention_static": (_I32, [_P, _I32, ctypes.POINTER(ba_ring), ctypes.POINTER(ba_ring),
                                          ctypes.POINTER(ba_block_meta), _I32, ctypes.c_float, _P, _P, _P]),
     "ba_attention_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
+    "ba_text_ring_set": (_I32, [ctypes.POINTER(ba_ring), _I32, _P, _P, _I32, _I32, _P]),
+    "ba_block_attention_text_arrays": (_I32, [_P, _I32, ctypes.POINTER(ba_ring), _P, _P, _I32,
+                                              ctypes.POINTER(ba_block_meta), _I32, ctypes.c_float, _P, _P,
+                                              _P, ctypes.c_size_t, _P]),
+    "ba_attention_text_arrays_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "ba_attention_query_tile": (_I32, [_I32, _I32, _I32]),
     "ba_attention_plan": (_I32, [_I32, ctypes.POINTER(ba_ring), ctypes.POINTER(ba_ring),
                                  ctypes.POINTER(ba_block_meta), _I32, ctypes.c_size_t, ctypes.POINTER(_I32)]),
@@ -308,6 +313,59 @@ def ba_block_attention(q, cache, text, metas, scale=0.0, out=None, lse=None, wor
                                    _dev(lse, "lse") if lse is not None else None,
                                    ws_ptr, ws_bytes, _stream()),
            "ba_block_attention")
+    return out
+
+
+def ba_text_ring_set(text, text_k, text_v, text_len=None, slot=0):
+    """text_k, text_v: [heads][text_cap][head_dim] (head-major) in the ring's
+    dtype; tokens [0, text_len) (default: all text_cap) into slot `slot` of
+    the ring `text`, zeros after them."""
+    if text_k.dim() != 3 or text_k.shape != text_v.shape or text_k.dtype != text_v.dtype:
+        raise ValueError("text_k, text_v must be [heads][text_cap][head_dim] of one dtype")
+    cap = text_k.shape[1]
+    n = cap if text_len is None else int(text_len)
+    _check(_lib.ba_text_ring_set(ctypes.byref(text.desc), slot, _dev(text_k, "text_k"), _dev(text_v, "text_v"),
+                                 cap, n, _stream()), "ba_text_ring_set")
+
+
+def ba_attention_text_arrays_workspace_bytes(head_dim, dtype, n_blocks, q_stride, heads, text_cap):
+    return _lib.ba_attention_text_arrays_workspace_bytes(head_dim, dtype, n_blocks, q_stride, heads, text_cap)
+
+
+def ba_block_attention_text_arrays(q, cache, text_k, text_v, metas, workspace, scale=0.0, out=None, lse=None):
+    """ba_block_attention with the text K/V as [heads][text_cap][head_dim]
+    arrays (or None when no block reads text); workspace: a uint8 device
+    tensor of at least the text ring's bytes
+    (ba_attention_text_arrays_workspace_bytes gives the full size)."""
+    nb, q_stride = q.shape[0], q.shape[1]
+    if q.shape[2] != cache.desc.heads or q.shape[3] != cache.desc.head_dim:
+        raise ValueError("q shape does not match the cache ring")
+    if len(metas) != nb:
+        raise ValueError("one meta per block")
+    arr = (ba_block_meta * max(nb, 1))()
+    for i, m in enumerate(metas):
+        arr[i] = m if isinstance(m, ba_block_meta) else make_meta(
+            m["q_len"], m["segs"], m.get("text_slot", 0), m.get("text_len", 0))
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is not None and (lse.dtype != torch.float32 or lse.numel() < nb * cache.desc.heads * q_stride):
+        raise ValueError("lse must be fp32 [n_blocks][heads][q_stride]")
+    cap = 0
+    if text_k is not None:
+        if text_k.dim() != 3 or text_v is None or text_k.shape != text_v.shape:
+            raise ValueError("text_k, text_v must be [heads][text_cap][head_dim]")
+        cap = text_k.shape[1]
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    _check(_lib.ba_block_attention_text_arrays(
+        _dev(q, "q"), q_stride, ctypes.byref(cache.desc),
+        _dev(text_k, "text_k") if text_k is not None else None,
+        _dev(text_v, "text_v") if text_v is not None else None, cap,
+        arr, nb, float(scale), _dev(out, "out"), _dev(lse, "lse") if lse is not None else None,
+        ws_ptr, ws_bytes, _stream()), "ba_block_attention_text_arrays")
     return out
 
 

@@ -185,7 +185,7 @@ const char* ba_status_string(ba_status s) {
 
 const char* ba_last_error(void) { return g_err; }
 
-int32_t ba_version(void) { return 1 * 10000 + 3 * 100 + 0; }
+int32_t ba_version(void) { return 1 * 10000 + 4 * 100 + 0; }
 
 size_t ba_ring_bytes(int32_t n_slots, int32_t slot_tokens, int32_t heads, int32_t head_dim,
                      int32_t dtype) {
@@ -238,6 +238,8 @@ static ba_status append_common(const ba_ring* ring, const void* k, const void* v
     a.k = static_cast<const char*>(k) + first * block_elems * eb;
     a.v = static_cast<const char*>(v) + first * block_elems * eb;
     a.ring = ring->base;
+    a.src_tok = (int64_t)ring->heads * ring->head_dim;   // token-major [n_tokens][heads][head_dim]
+    a.src_head = ring->head_dim;
     a.n_tokens = n_tokens;
     a.heads = ring->heads;
     a.t_pad = ring->slot_stride_tokens;
@@ -539,6 +541,101 @@ ba_status ba_block_attention(const void* q, int32_t q_stride, const ba_ring* cac
     return fail(BA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   return attention_run(q, q_stride, cache, text, meta, n_blocks, scale, out, lse, workspace != nullptr,
                        workspace, workspace_bytes, stream, nullptr);
+}
+
+// ---- text K/V as plain arrays -------------------------------------------------
+
+ba_status ba_text_ring_set(const ba_ring* text, int32_t slot, const void* text_k, const void* text_v,
+                           int32_t text_cap, int32_t text_len, hipStream_t stream) {
+  ba_status st = check_ring(text, "text");
+  if (st != BA_OK) return st;
+  if (text_k == nullptr || text_v == nullptr) return fail(BA_ERR_INVALID_ARG, "text_k or text_v is NULL");
+  if (!aligned(text_k, 16) || !aligned(text_v, 16))
+    return fail(BA_ERR_INVALID_ARG, "text_k or text_v not 16-byte aligned");
+  if (slot < 0 || slot >= text->n_slots)
+    return fail(BA_ERR_OUT_OF_RANGE, "slot %d outside [0, %d)", slot, text->n_slots);
+  if (text_cap < 1 || (int64_t)text_cap * text->heads * text->head_dim >= ((int64_t)1 << 40))
+    return fail(BA_ERR_OUT_OF_RANGE, "text_cap %d out of range", text_cap);
+  if (text_len < 1 || text_len > text_cap || text_len > text->slot_tokens)
+    return fail(BA_ERR_OUT_OF_RANGE, "text_len %d outside [1, min(text_cap %d, slot_tokens %d)]", text_len,
+                text_cap, text->slot_tokens);
+  ba::AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = text_k;
+  a.v = text_v;
+  a.ring = text->base;
+  a.src_tok = text->head_dim;                           // head-major [heads][text_cap][head_dim]
+  a.src_head = (int64_t)text_cap * text->head_dim;
+  a.n_tokens = text_len;
+  a.heads = text->heads;
+  a.t_pad = text->slot_stride_tokens;
+  a.n_blocks = 1;
+  a.slot[0] = slot;
+  hipError_t e = ba::launch_append(a, text->head_dim, elem_bytes(text->dtype), stream);
+  if (e != hipSuccess) return hip_fail(e, "text copy launch");
+  return ok();
+}
+
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t ba_attention_text_arrays_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_blocks,
+                                                int32_t q_stride, int32_t heads, int32_t text_cap) {
+  const size_t ring = ba_ring_bytes(1, text_cap, heads, head_dim, dtype);
+  if (ring == 0) return 0;
+  return round256(ring) + ba_attention_workspace_bytes(head_dim, dtype, n_blocks, q_stride, heads);
+}
+
+ba_status ba_block_attention_text_arrays(const void* q, int32_t q_stride, const ba_ring* cache,
+                                         const void* text_k, const void* text_v, int32_t text_cap,
+                                         const ba_block_meta* meta, int32_t n_blocks, float scale, void* out,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  if (q == nullptr || out == nullptr) return fail(BA_ERR_INVALID_ARG, "q or out is NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(BA_ERR_INVALID_ARG, "q or out not 16-byte aligned");
+  if (lse != nullptr && !aligned(lse, 4)) return fail(BA_ERR_INVALID_ARG, "lse not 4-byte aligned");
+  if (workspace != nullptr && !aligned(workspace, 256))
+    return fail(BA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  ba_status st = check_ring(cache, "cache");
+  if (st != BA_OK) return st;
+  if (n_blocks > 0 && meta == nullptr) return fail(BA_ERR_INVALID_ARG, "meta is NULL");
+  int32_t max_len = 0;
+  for (int b = 0; b < n_blocks; ++b)
+    if (meta[b].text_len > max_len) max_len = meta[b].text_len;
+  if (max_len == 0)   // no block reads the text: plain block attention
+    return attention_run(q, q_stride, cache, nullptr, meta, n_blocks, scale, out, lse, workspace != nullptr,
+                         workspace, workspace_bytes, stream, nullptr);
+  if (text_k == nullptr || text_v == nullptr) return fail(BA_ERR_INVALID_ARG, "text_len > 0 but text_k or text_v is NULL");
+  if (!aligned(text_k, 16) || !aligned(text_v, 16))
+    return fail(BA_ERR_INVALID_ARG, "text_k or text_v not 16-byte aligned");
+  const size_t ring = ba_ring_bytes(1, text_cap, cache->heads, cache->head_dim, cache->dtype);
+  if (ring == 0) return fail(BA_ERR_OUT_OF_RANGE, "text_cap %d out of range", text_cap);
+  const size_t rb = round256(ring);
+  if (workspace == nullptr || workspace_bytes < rb)
+    return fail(BA_ERR_INVALID_ARG, "workspace of %zu bytes cannot hold the text ring (%zu bytes)",
+                workspace == nullptr ? (size_t)0 : workspace_bytes, rb);
+  // the text ring at the start of the workspace, the rest for the split
+  // schedule's partial results
+  ba_ring tr;
+  memset(&tr, 0, sizeof(tr));
+  tr.base = workspace;
+  tr.n_slots = 1;
+  tr.slot_tokens = text_cap;
+  tr.heads = cache->heads;
+  tr.head_dim = cache->head_dim;
+  tr.dtype = cache->dtype;
+  tr.slot_stride_tokens = (int32_t)pad_tokens(text_cap);
+  void* rest = workspace_bytes > rb ? static_cast<char*>(workspace) + rb : nullptr;
+  const size_t rest_bytes = workspace_bytes > rb ? workspace_bytes - rb : 0;
+  // every check of the attention call (key sets, text_len <= text_cap,
+  // text_slot 0) before anything is launched
+  int32_t plan = 0;
+  st = attention_run(q, q_stride, cache, &tr, meta, n_blocks, scale, out, lse, rest != nullptr, rest, rest_bytes,
+                     stream, &plan);
+  if (st != BA_OK) return st;
+  st = ba_text_ring_set(&tr, 0, text_k, text_v, text_cap, max_len, stream);
+  if (st != BA_OK) return st;
+  return attention_run(q, q_stride, cache, &tr, meta, n_blocks, scale, out, lse, rest != nullptr, rest, rest_bytes,
+                       stream, nullptr);
 }
 
 ba_status ba_attention_plan(int32_t q_stride, const ba_ring* cache, const ba_ring* text,

@@ -1,5 +1,6 @@
-// Cache append: one block's K/V (token-major, as a QKV projection emits them)
-// into a ring slot.  K keeps its token-major rows; V is transposed to the
+// Cache append: one block's K/V (token-major, as a QKV projection emits them,
+// or head-major, as a text prompt's per-head K/V arrays come) into a ring
+// slot.  K keeps its token-major rows; V is transposed to the
 // dim-major layout the attention kernel streams.  Pure data movement, bound by
 // HBM bandwidth: every byte is read once and written once, 16 bytes per lane.
 //
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const AppendArgs a) {
     const int t = t0 + g / ROW_CH;
     const int c = g % ROW_CH;
     u32x4 val = {0u, 0u, 0u, 0u};
-    if (t < a.n_tokens) val = load_stream(ksrc + ((int64_t)t * H + h) * D + c * (16 / EB));
+    if (t < a.n_tokens) val = load_stream(ksrc + t * a.src_tok + h * a.src_head + c * (16 / EB));
     if (t < a.t_pad) *reinterpret_cast<u32x4*>(kdst + (int64_t)t * D + c * (16 / EB)) = val;
   }
 
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const AppendArgs a) {
     const int t = t0 + tl;
     const int c = g % ROW_CH;
     u32x4 val = {0u, 0u, 0u, 0u};
-    if (t < a.n_tokens) val = load_stream(vsrc + ((int64_t)t * H + h) * D + c * (16 / EB));
+    if (t < a.n_tokens) val = load_stream(vsrc + t * a.src_tok + h * a.src_head + c * (16 / EB));
     unsigned int* dst = reinterpret_cast<unsigned int*>(vt + tl * LROW + c * (16 / EB));
     dst[0] = val[0]; dst[1] = val[1]; dst[2] = val[2]; dst[3] = val[3];
   }

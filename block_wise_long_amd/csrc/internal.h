@@ -20,9 +20,11 @@ constexpr int64_t kAttnMaxSlotStride = (int64_t)1 << 26;
 
 // ---- ring append -----------------------------------------------------------
 struct AppendArgs {
-  const void* k;            // [n_blocks][n_tokens][heads][D]
+  const void* k;            // block z's token t, head h at z*n_tokens*heads*D + t*src_tok + h*src_head
   const void* v;
   void* ring;               // ring base
+  int64_t src_tok;          // elements between tokens: heads*D token-major, D head-major
+  int64_t src_head;         // elements between heads: D token-major, cap*D head-major
   int32_t n_tokens;
   int32_t heads;
   int32_t t_pad;            // slot token stride

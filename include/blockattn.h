@@ -143,9 +143,11 @@ typedef struct {
  *          i >= q_len of a block are neither read nor written.  out may be q.
  * cache:   the K/V ring; text: a ring with the text K/V (same heads,
  *          head_dim, dtype), or NULL when every text_len is 0.  The text
- *          K/V is passed as a ring (appended once per prompt with
- *          ba_cache_append; meta[b].text_slot picks the slot) rather than as
- *          plain [heads][text_len][head_dim] arrays: a ring matrix stores V
+ *          K/V is passed as a ring (filled once per prompt with
+ *          ba_cache_append, or from [heads][text_cap][head_dim] arrays with
+ *          ba_text_ring_set; meta[b].text_slot picks the slot) rather than
+ *          as plain arrays (ba_block_attention_text_arrays takes those and
+ *          fills a ring in its workspace first): a ring matrix stores V
  *          transposed ([head_dim][T_pad] per head), which is the layout the
  *          PV product streams from, so the text keys take the same path
  *          through the kernel as the cached segments, with no per-call
@@ -204,6 +206,50 @@ ba_status ba_block_attention_static(const void* q, int32_t q_stride, const ba_ri
  * sharing the split. */
 size_t ba_attention_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_blocks,
                                     int32_t q_stride, int32_t heads);
+
+/*
+ * The text part of the key set (the text K/V every block of a call attends
+ * to besides its cache segments; DualParal Abstract, pith.science verdict,
+ * core_discovery) given as plain arrays: text_k, text_v are
+ * [heads][text_cap][head_dim] in the ring's dtype, head-major, 16-byte
+ * aligned.  Tokens [0, text_len) go into slot `slot` of the ring `text`
+ * (K rows as they are, V transposed to the ring's layout) and tokens
+ * [text_len, T_pad) of that slot become zeros; text->appended is unchanged.
+ * 1 <= text_len <= min(text_cap, text->slot_tokens).  One launch; pure data
+ * movement (the slot holds the exact bits afterwards).
+ */
+ba_status ba_text_ring_set(const ba_ring* text, int32_t slot, const void* text_k,
+                           const void* text_v, int32_t text_cap, int32_t text_len,
+                           hipStream_t stream);
+
+/*
+ * ba_block_attention with the text K/V as plain arrays (as for
+ * ba_text_ring_set; NULL allowed when every text_len is 0) instead of a text
+ * ring: every meta[b].text_slot must be 0 and text_len <= text_cap.  The
+ * call writes the text (the longest text_len of the call) into a one-slot
+ * ring at the start of `workspace`, then runs ba_block_attention on it with
+ * the rest of the workspace for the split schedule's partial results.  The
+ * workspace (256-byte aligned, caller-owned, no initialisation needed) must
+ * hold the ring when any text_len > 0: ba_attention_text_arrays_workspace_bytes
+ * gives the ring plus a full ba_attention_workspace_bytes; any size from the
+ * ring's up works, with fewer tail workgroups.  Every check of both steps
+ * runs before either launch.  Results are those of ba_block_attention on a
+ * ring filled with the same text.  Callers that keep one prompt for many
+ * calls save the per-call text copy by filling a text ring once
+ * (ba_text_ring_set) and calling ba_block_attention.
+ */
+ba_status ba_block_attention_text_arrays(const void* q, int32_t q_stride, const ba_ring* cache,
+                                         const void* text_k, const void* text_v,
+                                         int32_t text_cap, const ba_block_meta* meta,
+                                         int32_t n_blocks, float scale, void* out, float* lse,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/* Workspace bytes for ba_block_attention_text_arrays on the current device:
+ * the one-slot text ring of text_cap tokens (rounded up to 256 bytes), then
+ * ba_attention_workspace_bytes.  0 for a bad shape. */
+size_t ba_attention_text_arrays_workspace_bytes(int32_t head_dim, int32_t dtype, int32_t n_blocks,
+                                                int32_t q_stride, int32_t heads, int32_t text_cap);
 
 /* Queries of one head that one workgroup of ba_block_attention takes (its
  * query tile) in a launch whose longest key set (cache segments + text) has

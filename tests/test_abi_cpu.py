@@ -21,11 +21,11 @@ FAKE = 0x7F0000000000        # 256-byte aligned dummy device address, never dere
 
 def test_exports_every_declared_symbol():
     names = B.header_symbols()
-    assert len(names) == 22
+    assert len(names) == 25
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert B.ba_version() == 10300
+    assert B.ba_version() == 10400
 
 
 @pytest.mark.parametrize("shape", [(2, 5400, 24, 64), (16, 5400, 24, 64), (2, 7800, 40, 128), (1, 226, 24, 64),
@@ -175,6 +175,49 @@ def test_attention_rejects():
     assert "head_dim" in B.ba_last_error()
     assert _attn(c, None, [_meta()], ws=FAKE + 64, ws_bytes=1 << 20) == B.BA_ERR_INVALID_ARG
     assert "workspace" in B.ba_last_error()
+
+
+def test_text_arrays_reject_before_any_launch():
+    # the text K/V as [heads][text_cap][head_dim] arrays: the copy into a
+    # text ring and the attention call that makes that ring in its workspace
+    f = B.raw.ba_text_ring_set
+    t = _ring(1, 100)
+    tr = ctypes.byref(t)
+    assert f(tr, 0, None, FAKE, 120, 50, None) == B.BA_ERR_INVALID_ARG
+    assert f(tr, 0, FAKE, FAKE + 8, 120, 50, None) == B.BA_ERR_INVALID_ARG
+    assert f(tr, 1, FAKE, FAKE, 120, 50, None) == B.BA_ERR_OUT_OF_RANGE      # slot
+    assert f(tr, 0, FAKE, FAKE, 120, 0, None) == B.BA_ERR_OUT_OF_RANGE       # text_len
+    assert f(tr, 0, FAKE, FAKE, 40, 50, None) == B.BA_ERR_OUT_OF_RANGE       # text_len > text_cap
+    assert f(tr, 0, FAKE, FAKE, 120, 101, None) == B.BA_ERR_OUT_OF_RANGE     # text_len > slot_tokens
+    assert f(tr, 0, FAKE, FAKE, 0, 1, None) == B.BA_ERR_OUT_OF_RANGE         # text_cap
+    bad = _ring(1, 100); bad.slot_stride_tokens = 100
+    assert f(ctypes.byref(bad), 0, FAKE, FAKE, 120, 50, None) == B.BA_ERR_INVALID_ARG
+
+    c = _ring()
+    cap = 30
+    ring_bytes = -(-B.ba_ring_bytes(1, cap, 2, 64, B.BA_BF16) // 256) * 256
+    assert B.ba_attention_text_arrays_workspace_bytes(64, B.BA_BF16, 1, 16, 2, cap) == \
+        ring_bytes + B.ba_attention_workspace_bytes(64, B.BA_BF16, 1, 16, 2)
+    assert B.ba_attention_text_arrays_workspace_bytes(96, B.BA_BF16, 1, 16, 2, cap) == 0
+    assert B.ba_attention_text_arrays_workspace_bytes(64, B.BA_BF16, 1, 16, 2, 0) == 0
+
+    def attn(metas, tk=FAKE, tv=FAKE, text_cap=cap, ws=FAKE, ws_bytes=ring_bytes, q=FAKE):
+        arr = (B.ba_block_meta * len(metas))(*metas)
+        return B.raw.ba_block_attention_text_arrays(q, 16, ctypes.byref(c), tk, tv, text_cap, arr, len(metas), 0.0,
+                                                    FAKE, None, ws, ws_bytes, None)
+    assert attn([_meta(text_len=3)], tk=None) == B.BA_ERR_INVALID_ARG
+    assert attn([_meta(text_len=3)], tv=FAKE + 8) == B.BA_ERR_INVALID_ARG
+    assert attn([_meta(text_len=3)], ws=None, ws_bytes=0) == B.BA_ERR_INVALID_ARG
+    assert "text ring" in B.ba_last_error()
+    assert attn([_meta(text_len=3)], ws_bytes=ring_bytes - 1) == B.BA_ERR_INVALID_ARG
+    assert attn([_meta(text_len=3)], ws=FAKE + 64) == B.BA_ERR_INVALID_ARG               # alignment
+    assert attn([_meta(text_len=cap + 1)]) == B.BA_ERR_OUT_OF_RANGE                       # text_len > text_cap
+    assert attn([_meta(text_len=3, text_slot=1)]) == B.BA_ERR_OUT_OF_RANGE
+    assert attn([_meta(text_len=3)], text_cap=0) == B.BA_ERR_OUT_OF_RANGE
+    assert attn([_meta(text_len=3), _meta(segs=((2, 5),))]) == B.BA_ERR_OUT_OF_RANGE     # a cache slot
+    assert attn([_meta(text_len=3)], q=FAKE + 2) == B.BA_ERR_INVALID_ARG
+    # no block reads text: the arrays may be absent, the plain call's checks apply
+    assert attn([_meta(segs=((2, 5),))], tk=None, tv=None, ws=None, ws_bytes=0) == B.BA_ERR_OUT_OF_RANGE
 
 
 def test_static_attention_rejects_before_any_device_work():
