@@ -13,6 +13,9 @@
  *        Then the host bookkeeping, int32: the noise assignment of block 3
  *        (seed 7, pool 21, 3 excluded, 4 frames) and, for a 4-block queue
  *        (T 1000) at its third step, every block's write slot and timestep.
+ *        Last, uint16: out2 ([L][H][D]), the same attention through
+ *        ba_block_attention_text_arrays with the text given as
+ *        [H][TXT][D] arrays.
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -157,6 +160,28 @@ int main(int argc, char** argv) {
   CHECK_BA(ba_queue_plan(&q4, wslots, qm, tq, &stride));
   fwrite(wslots, 4, 4, f);
   fwrite(tq, 4, 4, f);
+
+  /* the same attention with the text as plain head-major arrays: the text
+     ring is made in the workspace */
+  uint16_t* kt_hm = (uint16_t*)malloc(tblk * 2);
+  uint16_t* vt_hm = (uint16_t*)malloc(tblk * 2);
+  for (int tk = 0; tk < TXT; ++tk)
+    for (int h = 0; h < H; ++h)
+      for (int d = 0; d < D; ++d) {
+        kt_hm[((size_t)h * TXT + tk) * D + d] = kt[((size_t)tk * H + h) * D + d];
+        vt_hm[((size_t)h * TXT + tk) * D + d] = vt[((size_t)tk * H + h) * D + d];
+      }
+  void *dkt_hm = to_device(kt_hm, tblk), *dvt_hm = to_device(vt_hm, tblk);
+  const size_t ws_bytes = ba_attention_text_arrays_workspace_bytes(D, BA_BF16, 1, L, H, TXT);
+  void *ws = NULL, *dout2 = NULL;
+  CHECK_HIP(hipMalloc(&ws, ws_bytes));
+  CHECK_HIP(hipMalloc(&dout2, blk * 2));
+  CHECK_BA(ba_block_attention_text_arrays(dq, L, &cache, dkt_hm, dvt_hm, TXT, &meta, 1, 0.0f, dout2, NULL, ws,
+                                          ws_bytes, stream));
+  CHECK_HIP(hipStreamSynchronize(stream));
+  uint16_t* out2 = (uint16_t*)malloc(blk * 2);
+  CHECK_HIP(hipMemcpy(out2, dout2, blk * 2, hipMemcpyDeviceToHost));
+  fwrite(out2, 2, blk, f);
   fclose(f);
   printf("abi_demo ok: slots ctx %d cur %d text %d, library %d\n", slot_ctx, slot_cur, slot_txt, ba_version());
   return 0;

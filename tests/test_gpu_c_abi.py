@@ -1,8 +1,9 @@
 """The library from plain C: tests/c/abi_demo (built by __graft_entry__.build()
 with gcc against the in-tree libblockattn.so and the HIP runtime, no Python,
 no torch in that process) appends a context block, the current block and the
-text, runs block attention and one DDIM update, and writes its inputs and
-outputs; they are checked here against the oracle."""
+text, runs block attention (with a text ring, and again with the text as
+plain arrays) and one DDIM update, and writes its inputs and outputs; they
+are checked here against the oracle."""
 import math
 import os
 import subprocess
@@ -37,8 +38,10 @@ def test_plain_c_caller(tmp_path):
     for n in sizes:
         parts.append(data[off:off + n])
         off += n
-    tail = np.frombuffer(raw[28 + 2 * sum(sizes):], dtype=np.int32)
-    assert tail.size == 12
+    rest = raw[28 + 2 * sum(sizes):]
+    tail = np.frombuffer(rest[:48], dtype=np.int32)
+    out2 = np.frombuffer(rest[48:], dtype=np.uint16)
+    assert tail.size == 12 and out2.size == L * H * D
     # host bookkeeping from C: the noise frames and the queue plan at step 2
     from oracle import noise as NZ
     from oracle import queue as OQ
@@ -57,6 +60,8 @@ def test_plain_c_caller(tmp_path):
     ref, _ = A.block_attention_ref(N.bf16_bits_to_f64(blk(q, L))[None], ring, text, meta)
     got = N.bf16_bits_to_f64(blk(out, L))[None]
     check_contract(got, ref, "bf16", gate2=False)
+    # the text as [H][TXT][D] arrays (ba_block_attention_text_arrays): the ring form's bits
+    assert np.array_equal(out2, out)
     rms = math.sqrt(np.nanmean(ref ** 2))
     assert np.nanmax(np.abs(got - ref)) <= 2 ** -7 * np.nanmax(np.abs(ref)) + 0.05 * rms
     # the update: within one bf16 ulp of the oracle's (plus the fp32 evaluation error)
