@@ -908,6 +908,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, Tile<D, S>::THREADS))) 
 // a (block, head) boundary runs one phase per key set: barrier, copy, barrier,
 // units dealt round-robin to the waves (wave i takes units i, i + NW, ...;
 // the hardware places wave i on SIMD i % 4, so the SIMDs get equal shares).
+// When that costs no extra round of units per wave, each (block, head) takes
+// whole workgroups instead and no range crosses (res_group_units).
 // Units are never cut: measured at 5400 queries x 24 heads, sharing the
 // left-over units' tiles among groups of waves (partial states folded in LDS
 // or through memory) was slower than letting one wave run a unit alone.
@@ -943,8 +945,22 @@ void attention_resident_kernel(const AttnArgs a) {
   }
   const int n_wg = 8 * a.wg_per_xcd;
   const int j = (blockIdx.x & 7) * a.wg_per_xcd + (blockIdx.x >> 3);
-  int pos = split_start(a.n_tasks, n_wg, j);
-  const int end = split_start(a.n_tasks, n_wg, j + 1);
+  int pos, end;
+  if (a.res_group_units > 0) {
+    // every (block, head) takes whole workgroups (consecutive ones, mostly
+    // on one XCD) that split its units evenly: no workgroup copies a second
+    // key set
+    const int nu = a.res_group_units;
+    const int G = a.n_tasks / nu;
+    const int g = split_owner(n_wg, G, j);
+    const int g0 = split_start(n_wg, G, g);
+    const int nk = split_start(n_wg, G, g + 1) - g0;
+    pos = g * nu + split_start(nu, nk, j - g0);
+    end = g * nu + split_start(nu, nk, j - g0 + 1);
+  } else {
+    pos = split_start(a.n_tasks, n_wg, j);
+    end = split_start(a.n_tasks, n_wg, j + 1);
+  }
   const bf16x8 sel = row_sum_selector(lane);
 
   while (pos < end) {

@@ -77,7 +77,7 @@ struct AttnArgs {
   int32_t split;
   int32_t n_blocks;
   int32_t merge_per_xcd;    // merge workgroups per XCD (split)
-  int32_t pad_;
+  int32_t res_group_units;  // resident shape: units per (block, head) when each takes whole workgroups, else 0
   AttnBlock blk[kAttnMaxBlocks];
 };
 hipError_t launch_attention_bf16(const AttnArgs& a, int head_dim, int shape, hipStream_t s);

@@ -193,3 +193,28 @@ def test_eight_segments_in_one_resident_key_set():
     _bar(got[:, rows][:, :, heads], ref[:, rows][:, :, heads])
     sel = ~np.isnan(ref_lse)
     assert np.max(np.abs(lse.cpu().numpy()[sel] - ref_lse[sel])) < 2e-3
+
+
+def test_per_head_workgroups_same_bits_as_contiguous_ranges():
+    # one 480p block over a 512-key text: each of its 24 heads takes whole
+    # workgroups (no workgroup copies two key sets); the same block beside a
+    # block of another query count is cut into contiguous ranges that cross
+    # heads.  A unit's arithmetic does not depend on the workgroup that runs
+    # it, so the block's outputs and log-sum-exps agree bit for bit.
+    import torch
+    rng = _rng(87)
+    H, D, L, TXT = 24, 64, 5400, 512
+    _resident(H * ((L + 31) // 32))
+    w = Workload("bf16", 1, 64, H, D, TXT)
+    w.set_text(draw(rng, (TXT, H, D), 0.5, "bf16"), draw(rng, (TXT, H, D), 0.5, "bf16"))
+    m0 = {"q_len": L, "segs": [], "text_slot": 0, "text_len": TXT}
+    m1 = {"q_len": 1000, "segs": [], "text_slot": 0, "text_len": TXT}
+    q = draw(rng, (2, L, H, D), 0.5, "bf16")
+    out_a, lse_a = w.run(q[:1], [m0], workspace=None)
+    out_c, lse_c = w.run(q, [m0, m1], workspace=None)
+    assert torch.equal(out_a[0].view(torch.int16), out_c[0].view(torch.int16))
+    assert torch.equal(lse_a[0].view(torch.int32), lse_c[0].view(torch.int32))
+    heads, rows = [0, 12, 23], sorted(set(range(0, L, 59)) | set(range(L - 8, L)))
+    ref, _ = w.oracle(q[:1], [m0], heads=heads, rows=rows)
+    got = decode(out_a, "bf16")
+    _bar(got[:, rows][:, :, heads], ref[:, rows][:, :, heads])
