@@ -111,3 +111,34 @@ def test_projection_and_text_cross_attention_in_a_graph():
     eager = [o.clone() for o in run()]
     torch.cuda.synchronize()
     _replay_matches(run, state, eager)
+
+
+def test_static_entry_in_a_graph():
+    # the entry point that allocates nothing, meant for code under capture:
+    # a 480p block on the split schedule (tail workgroups, the library's own
+    # scratch array, the merge kernel) recorded once and replayed
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    L, H, D, TXT = 5400, 24, 64, 226
+    ring = B.ba_ring_init(2, L, H, D, B.BA_BF16)
+    text = B.ba_ring_init(1, TXT, H, D, B.BA_BF16)
+    for _ in range(2):
+        B.ba_cache_append(ring, _randn(gen, (L, H, D), 0.5), _randn(gen, (L, H, D), 0.5), L)
+    B.ba_cache_append(text, _randn(gen, (TXT, H, D), 0.5), _randn(gen, (TXT, H, D), 0.5), TXT)
+    q = _randn(gen, (1, L, H, D), 0.5)
+    metas = [{"q_len": L, "segs": [(0, L), (1, L)], "text_slot": 0, "text_len": TXT}]
+    out = torch.empty_like(q)
+    lse = torch.empty((1, H, L), dtype=torch.float32, device="cuda")
+    ws = B.attention_workspace(D, B.BA_BF16, 1, L, H)
+    assert B.ba_attention_plan(L, ring, text, metas, ws.numel()) > 0      # split schedule
+
+    def run():
+        B.ba_block_attention_static(q, ring, text, metas, out=out, lse=lse)
+        return [out, lse]
+
+    eager = [o.clone() for o in run()]
+    ref = B.ba_block_attention(q, ring, text, metas, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(eager[0].view(torch.int16), ref.view(torch.int16))
+    state = [(out, out.clone()), (lse, lse.clone())]
+    _replay_matches(run, state, eager)
